@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for hybrid paged GQA attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library never uses it, and this
+package imports nothing from the library.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+(query, head)); this wrapper only builds it with gcc and marshals numpy arrays.
+Citations for what is computed are in ``oracle.c``'s header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+OK, BAD_ARG, MISSING_KEYS, NO_MEM = 0, -1, -2, -3
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP)."""
+    stale = (not os.path.exists(_LIB) or
+             os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC), os.path.getmtime(_HDR)))
+    if force or stale:
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            i32p = ctypes.POINTER(ctypes.c_int32)
+            u16p = ctypes.POINTER(ctypes.c_uint16)
+            f64p = ctypes.POINTER(ctypes.c_double)
+            c_int, c_double = ctypes.c_int, ctypes.c_double
+            lib.oracle_attend.restype = c_int
+            lib.oracle_attend.argtypes = [c_int, c_int, c_int, c_int, c_int, c_double, c_int,
+                                          i32p, i32p, i32p, u16p, u16p, u16p, f64p, f64p]
+            lib.oracle_decode_split.restype = c_int
+            lib.oracle_decode_split.argtypes = [c_int, c_int, c_int, c_int, c_int, c_double, c_int,
+                                                i32p, i32p, u16p, u16p, u16p, c_int, f64p, f64p]
+            lib.oracle_layer_is_global.restype = c_int
+            lib.oracle_layer_is_global.argtypes = [c_int, c_int]
+            lib.oracle_threads.restype = c_int
+            lib.oracle_threads.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype)) if a is not None else None
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _u16(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.uint16)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def attend(is_global: bool, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int,
+           scale: float, q_lens, ctx_lens, k_starts, q, k, v=None):
+    """Exact-definition attention in fp64. Returns (out [T][Hq][hd], lse [T][Hq])."""
+    lib = _load()
+    q_lens, ctx_lens = _i32(q_lens), _i32(ctx_lens)
+    k_starts = None if k_starts is None else _i32(k_starts)
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    T = int(q_lens.sum())
+    out = np.empty((T, num_q_heads, head_dim), dtype=np.float64)
+    lse = np.empty((T, num_q_heads), dtype=np.float64)
+    rc = lib.oracle_attend(int(bool(is_global)), num_q_heads, num_kv_heads, head_dim, int(window),
+                           float(scale), int(q_lens.shape[0]), _ptr(q_lens, ctypes.c_int32),
+                           _ptr(ctx_lens, ctypes.c_int32), _ptr(k_starts, ctypes.c_int32),
+                           _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+                           _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != OK:
+        raise OracleError(f"oracle_attend failed: {rc}")
+    return out, lse
+
+
+def decode_split(is_global: bool, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int,
+                 scale: float, ctx_lens, k_starts, q, k, v, split_tokens: int):
+    """Split-KV decode merged by logsumexp, in fp64. Returns (out [B][Hq][hd], lse [B][Hq])."""
+    lib = _load()
+    ctx_lens = _i32(ctx_lens)
+    k_starts = None if k_starts is None else _i32(k_starts)
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B = int(ctx_lens.shape[0])
+    out = np.empty((B, num_q_heads, head_dim), dtype=np.float64)
+    lse = np.empty((B, num_q_heads), dtype=np.float64)
+    rc = lib.oracle_decode_split(int(bool(is_global)), num_q_heads, num_kv_heads, head_dim, int(window),
+                                 float(scale), B, _ptr(ctx_lens, ctypes.c_int32),
+                                 _ptr(k_starts, ctypes.c_int32), _ptr(q, ctypes.c_uint16),
+                                 _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16), int(split_tokens),
+                                 _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != OK:
+        raise OracleError(f"oracle_decode_split failed: {rc}")
+    return out, lse
+
+
+def layer_is_global(layer: int, n_layers: int) -> int:
+    return _load().oracle_layer_is_global(int(layer), int(n_layers))
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def attend_batch(batch, rows=None):
+    """Run ``attend`` on a ``workloads.Batch`` (all rows, or a subset). Contiguous side only."""
+    b = batch if rows is None else batch.subset(rows)
+    s = b.spec
+    return attend(s.is_global, s.num_q_heads, s.num_kv_heads, s.head_dim, s.window,
+                  s.softmax_scale, b.q_lens, b.ctx_lens, b.k_starts, b.q, b.k, b.v)

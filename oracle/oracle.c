@@ -1,0 +1,313 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for hybrid paged GQA attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the library's compute path may call, link
+ * or load this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * What it computes is the plain definition of softmax attention, restricted by
+ * the two masks the pages describe (pegainfer issue "[Model] Gemma 4 M1 12B",
+ * Description: local sliding-window attention at head_dim 256 and global
+ * attention at head_dim 512, GQA with two KV head counts, paged prefill and
+ * decode; Core AI card, section "hybrid-pf64/ bundles": block-GQA head mapping
+ * and a decode step whose single query attends the whole grown cache).
+ *
+ *   query position p (absolute, from 0); query head h; KV head kv = floor(h / g)
+ *   visible keys  J(p) = { j : lo(p) <= j <= p },
+ *                 lo(p) = 0 (global) or max(0, p - W + 1) (local: the last W
+ *                 positions, the current one included)
+ *   scores        s_j = scale * sum_d q[p,h,d] * K[j,kv,d]
+ *   logsumexp     LSE = m + ln sum_j exp(s_j - m),  m = max_j s_j
+ *   output        O[p,h,:] = sum_j exp(s_j - LSE) * V[j,kv,:]
+ *
+ * The softmax is two-pass (max, then sum) with no online rescaling. Inputs are
+ * bfloat16 bit patterns widened exactly to double; all arithmetic is double.
+ * K and V are contiguous per row (no pages): row r stores tokens
+ * [k_start[r], ctx_len[r]) back to back as [token][kv_head][head_dim].
+ *
+ * The split-KV routine follows the pegainfer "[Model] Gemma 4 M3 31B" plan's
+ * split-KV chunk policy in its plainest reading: cut a row's keys at absolute
+ * multiples of the split size, attend each piece on its own, then merge the
+ * pieces by their logsumexp. It exists only to check that the merge is exact.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <string.h>
+
+static double widen_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* First key position visible to a query at position p. */
+static int64_t visible_lo(int is_global, int window, int64_t p)
+{
+    if (is_global)
+        return 0;
+    int64_t lo = p - (int64_t)window + 1;
+    return lo > 0 ? lo : 0;
+}
+
+typedef struct {
+    int is_global, Hq, Hkv, hd, window;
+    double scale;
+    int B;
+    const int32_t *q_lens, *ctx_lens, *k_starts;
+    const uint16_t *q, *k, *v;
+    int64_t *q_off;   /* [B+1] first query index of each row */
+    int64_t *k_off;   /* [B]   first stored token index of each row */
+} problem;
+
+static int check_and_index(problem *pb)
+{
+    if (pb->Hq <= 0 || pb->Hkv <= 0 || pb->hd <= 0 || pb->B < 0)
+        return ORACLE_BAD_ARG;
+    if (pb->Hq % pb->Hkv != 0)
+        return ORACLE_BAD_ARG;
+    if (!pb->is_global && pb->window < 1)
+        return ORACLE_BAD_ARG;
+    pb->q_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(pb->B + 1));
+    pb->k_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(pb->B + 1));
+    if (!pb->q_off || !pb->k_off)
+        return ORACLE_NO_MEM;
+    int64_t qo = 0, ko = 0;
+    for (int r = 0; r < pb->B; ++r) {
+        int64_t L = pb->ctx_lens[r], C = pb->q_lens[r], k0 = pb->k_starts ? pb->k_starts[r] : 0;
+        if (C < 0 || L < C || k0 < 0 || k0 > L)
+            return ORACLE_BAD_ARG;
+        if (C > 0 && L < 1)
+            return ORACLE_BAD_ARG;
+        /* every key a query of this row can see must be stored */
+        if (C > 0 && visible_lo(pb->is_global, pb->window, L - C) < k0)
+            return ORACLE_MISSING_KEYS;
+        pb->q_off[r] = qo;
+        pb->k_off[r] = ko;
+        qo += C;
+        ko += L - k0;
+    }
+    pb->q_off[pb->B] = qo;
+    pb->k_off[pb->B] = ko;
+    return ORACLE_OK;
+}
+
+static int row_of_query(const problem *pb, int64_t t)
+{
+    int lo = 0, hi = pb->B - 1;
+    while (lo < hi) {              /* last row with q_off[row] <= t */
+        int mid = (lo + hi + 1) / 2;
+        if (pb->q_off[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+static const uint16_t *key_ptr(const problem *pb, const uint16_t *base, int r, int64_t j, int kv)
+{
+    int64_t k0 = pb->k_starts ? pb->k_starts[r] : 0;
+    return base + ((pb->k_off[r] + (j - k0)) * pb->Hkv + kv) * (int64_t)pb->hd;
+}
+
+/* Attend keys [a, b] (inclusive) of row r for one query vector; two-pass softmax.
+ * Writes the normalised output (hd doubles) and returns the logsumexp. */
+static double attend_range(const problem *pb, int r, int kv, const double *qv,
+                           int64_t a, int64_t b, double *scores, double *o)
+{
+    const int hd = pb->hd;
+    int64_t n = b - a + 1;
+    double m = -INFINITY;
+    for (int64_t j = a; j <= b; ++j) {
+        const uint16_t *kr = key_ptr(pb, pb->k, r, j, kv);
+        double dot = 0.0;
+        for (int d = 0; d < hd; ++d)
+            dot += qv[d] * widen_bf16(kr[d]);
+        double s = pb->scale * dot;
+        scores[j - a] = s;
+        if (s > m)
+            m = s;
+    }
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        sum += exp(scores[i] - m);
+    double lse = m + log(sum);
+    for (int d = 0; d < hd; ++d)
+        o[d] = 0.0;
+    for (int64_t j = a; j <= b; ++j) {
+        double w = exp(scores[j - a] - lse);
+        const uint16_t *vr = key_ptr(pb, pb->v, r, j, kv);
+        for (int d = 0; d < hd; ++d)
+            o[d] += w * widen_bf16(vr[d]);
+    }
+    return lse;
+}
+
+int oracle_attend(int is_global, int Hq, int Hkv, int hd, int window, double scale,
+                  int B, const int32_t *q_lens, const int32_t *ctx_lens, const int32_t *k_starts,
+                  const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  double *out, double *lse)
+{
+    problem pb = {is_global, Hq, Hkv, hd, window, scale, B, q_lens, ctx_lens, k_starts,
+                  q, k, v ? v : k, NULL, NULL};
+    int rc = check_and_index(&pb);
+    if (rc != ORACLE_OK) {
+        free(pb.q_off);
+        free(pb.k_off);
+        return rc;
+    }
+    const int g = Hq / Hkv;
+    const int64_t T = pb.q_off[B];
+    int64_t max_keys = 1;
+    for (int r = 0; r < B; ++r)
+        if (ctx_lens[r] > max_keys)
+            max_keys = ctx_lens[r];
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)max_keys);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)hd);
+        int ok = scores && qv;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t item = 0; item < T * Hq; ++item) {
+                if (!ok)
+                    continue;
+                int64_t t = item / Hq;
+                int h = (int)(item % Hq);
+                int r = row_of_query(&pb, t);
+                int64_t p = (int64_t)ctx_lens[r] - q_lens[r] + (t - pb.q_off[r]);
+                int kv = h / g;
+                for (int d = 0; d < hd; ++d)
+                    qv[d] = widen_bf16(q[(t * Hq + h) * (int64_t)hd + d]);
+                lse[t * Hq + h] = attend_range(&pb, r, kv, qv, visible_lo(is_global, window, p), p,
+                                               scores, out + (t * Hq + h) * (int64_t)hd);
+            }
+        }
+        free(scores);
+        free(qv);
+    }
+    free(pb.q_off);
+    free(pb.k_off);
+    return failed ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+int oracle_decode_split(int is_global, int Hq, int Hkv, int hd, int window, double scale,
+                        int B, const int32_t *ctx_lens, const int32_t *k_starts,
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int split_tokens, double *out, double *lse)
+{
+    if (split_tokens < 1)
+        return ORACLE_BAD_ARG;
+    int32_t *ones = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+    if (!ones)
+        return ORACLE_NO_MEM;
+    for (int r = 0; r < B; ++r)
+        ones[r] = 1;
+    problem pb = {is_global, Hq, Hkv, hd, window, scale, B, ones, ctx_lens, k_starts,
+                  q, k, v ? v : k, NULL, NULL};
+    int rc = check_and_index(&pb);
+    if (rc != ORACLE_OK) {
+        free(pb.q_off);
+        free(pb.k_off);
+        free(ones);
+        return rc;
+    }
+    const int g = Hq / Hkv;
+    int64_t max_keys = 1;
+    for (int r = 0; r < B; ++r)
+        if (ctx_lens[r] > max_keys)
+            max_keys = ctx_lens[r];
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)max_keys);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)hd);
+        double *part_o = (double *)malloc(sizeof(double) * (size_t)hd);
+        int64_t max_parts = max_keys / split_tokens + 2;
+        double *lse_parts = (double *)malloc(sizeof(double) * (size_t)max_parts);
+        double *o_parts = (double *)malloc(sizeof(double) * (size_t)(max_parts * hd));
+        int ok = scores && qv && part_o && lse_parts && o_parts;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t item = 0; item < (int64_t)B * Hq; ++item) {
+                if (!ok)
+                    continue;
+                int r = (int)(item / Hq), h = (int)(item % Hq), kv = h / g;
+                int64_t p = (int64_t)ctx_lens[r] - 1;
+                int64_t lo = visible_lo(is_global, window, p);
+                for (int d = 0; d < hd; ++d)
+                    qv[d] = widen_bf16(q[item * (int64_t)hd + d]);
+                /* pieces: keys [s*S, (s+1)*S) intersected with [lo, p] */
+                int np = 0;
+                for (int64_t s = lo / split_tokens; s * split_tokens <= p; ++s) {
+                    int64_t a = s * split_tokens, b = a + split_tokens - 1;
+                    if (a < lo) a = lo;
+                    if (b > p) b = p;
+                    lse_parts[np] = attend_range(&pb, r, kv, qv, a, b, scores, o_parts + np * (int64_t)hd);
+                    ++np;
+                }
+                /* merge by logsumexp */
+                double M = -INFINITY;
+                for (int i = 0; i < np; ++i)
+                    if (lse_parts[i] > M)
+                        M = lse_parts[i];
+                double sum = 0.0;
+                for (int i = 0; i < np; ++i)
+                    sum += exp(lse_parts[i] - M);
+                double L = M + log(sum);
+                double *o = out + item * (int64_t)hd;
+                for (int d = 0; d < hd; ++d)
+                    o[d] = 0.0;
+                for (int i = 0; i < np; ++i) {
+                    double w = exp(lse_parts[i] - L);
+                    for (int d = 0; d < hd; ++d)
+                        o[d] += w * o_parts[i * (int64_t)hd + d];
+                }
+                lse[item] = L;
+            }
+        }
+        free(scores);
+        free(qv);
+        free(part_o);
+        free(lse_parts);
+        free(o_parts);
+    }
+    free(pb.q_off);
+    free(pb.k_off);
+    free(ones);
+    return failed ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+int oracle_layer_is_global(int layer, int n_layers)
+{
+    /* Five local layers, then one global, repeated; the stack must end on a global layer. */
+    if (n_layers < 1 || n_layers % 6 != 0 || layer < 0 || layer >= n_layers)
+        return -1;
+    return (layer + 1) % 6 == 0 ? 1 : 0;
+}
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

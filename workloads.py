@@ -1,0 +1,292 @@
+"""Seeded synthetic inputs for hybrid paged GQA attention (Gemma-4-31B shapes).
+
+This module holds none of the attention arithmetic. It draws bf16 N(0,1) tensors,
+ragged context lengths and page tables, and scatters contiguous per-row K/V into
+the paged pool layout. Both sides of every parity check are fed from here: the
+HIP library reads the paged pool, the oracle reads the contiguous copy.
+
+Input recipe (stated once, used everywhere):
+  * Seeds: numpy ``SeedSequence([20261202, config, layer, tensor])`` feeding PCG64.
+    Tensor ids: 0 = Q, 1 = K, 2 = V, 3 = lengths, 4 = page permutation, 5 = priors.
+  * Values: ``standard_normal`` in float64, rounded to float32 (RNE), then to
+    bfloat16 (RNE on the float32 bits).
+  * Pool layout: ``[num_pages][num_kv_heads][page_size][head_dim]`` bf16, so one
+    (page, KV head) pair is a contiguous block. ``page_table[r][t // P]`` names
+    the page holding token t of row r; ``-1`` marks pages that are not backed.
+  * Page ids: every backed (row, logical page) pair gets a distinct physical page;
+    the assignment is a seeded global shuffle across all rows.
+
+Shapes follow the Gemma 4 31B description on the pegainfer issue pages (60 layers,
+five local layers per global one, "twice the attention heads", a different global
+KV head count) and the Core AI card's hybrid-pf64 section (32 query heads, 4 global
+KV heads at head_dim 512); the local family is 16 KV heads at head_dim 256 with a
+1024-token window.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+BASE_SEED = 20261202
+PAGE_SIZE = 16
+
+T_Q, T_K, T_V, T_LEN, T_PERM, T_PRIOR = range(6)
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# --------------------------------------------------------------------------- rng / bf16
+def generator(*key: int) -> np.random.Generator:
+    """PCG64 stream for one (config, layer, tensor) key."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, *[int(k) for k in key]])))
+
+
+def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); returns uint16 bits."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(gen: np.random.Generator, shape) -> np.ndarray:
+    """bf16 bits of N(0,1) draws: float64 -> float32 (RNE) -> bfloat16 (RNE)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16)
+    chunk = 1 << 24
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = f32_to_bf16_bits(gen.standard_normal(e - s).astype(np.float32))
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------- layer shapes
+@dataclass(frozen=True)
+class LayerSpec:
+    """One attention layer's geometry: family, head counts, window, page size, scale."""
+    family: str                 # "local" (sliding window) or "global" (full causal)
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int = 0             # keys visible to a query: the last `window` positions (local only)
+    kv_shared: bool = False     # V reads the K cache
+    scale: float = 0.0          # 0 -> 1/sqrt(head_dim)
+    page_size: int = PAGE_SIZE
+
+    @property
+    def is_global(self) -> bool:
+        return self.family == "global"
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale else 1.0 / math.sqrt(self.head_dim)
+
+
+LOCAL_31B = LayerSpec("local", 32, 16, 256, window=1024)
+GLOBAL_31B = LayerSpec("global", 32, 4, 512)
+GLOBAL_31B_KV_SHARED = LayerSpec("global", 32, 4, 512, kv_shared=True)
+
+
+# --------------------------------------------------------------------------- batches
+@dataclass
+class Batch:
+    """A ragged batch of rows for one layer, in both contiguous and paged form."""
+    spec: LayerSpec
+    ctx_lens: np.ndarray        # int32 [B]: tokens present in the cache, including this step's
+    q_lens: np.ndarray          # int32 [B]: queries per row (1 for decode)
+    k_starts: np.ndarray        # int32 [B]: first token stored contiguously (and backed) per row
+    q: np.ndarray               # uint16 [T][Hq][hd]
+    k: np.ndarray               # uint16 [sum(L - k_start)][Hkv][hd] contiguous rows
+    v: Optional[np.ndarray]     # same, or None when K=V
+    page_table: np.ndarray      # int32 [B][pt_stride]
+    k_pool: np.ndarray          # uint16 [num_pages][Hkv][P][hd]
+    v_pool: Optional[np.ndarray]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.ctx_lens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def pt_stride(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    def row_keys(self, r: int):
+        """Contiguous K (and V) of row r, tokens [k_start, L)."""
+        off = int(np.sum(self.ctx_lens[:r] - self.k_starts[:r]))
+        n = int(self.ctx_lens[r] - self.k_starts[r])
+        kk = self.k[off:off + n]
+        vv = kk if self.v is None else self.v[off:off + n]
+        return kk, vv
+
+    def subset(self, rows) -> "Batch":
+        """Contiguous-side view restricted to some rows (for sampled oracle checks)."""
+        rows = list(rows)
+        qs, ks, vs = [], [], []
+        cq = self.cu_q
+        for r in rows:
+            qs.append(self.q[cq[r]:cq[r + 1]])
+            kk, vv = self.row_keys(r)
+            ks.append(kk)
+            vs.append(vv)
+        return Batch(self.spec, self.ctx_lens[rows].copy(), self.q_lens[rows].copy(),
+                     self.k_starts[rows].copy(), np.concatenate(qs), np.concatenate(ks),
+                     None if self.v is None else np.concatenate(vs),
+                     self.page_table[rows].copy(), self.k_pool, self.v_pool, dict(self.meta))
+
+
+def first_needed_token(spec: LayerSpec, ctx_len: int, q_len: int) -> int:
+    """Earliest token any of the row's queries can see (0 for global rows)."""
+    if spec.is_global:
+        return 0
+    first_pos = ctx_len - q_len
+    return max(0, first_pos - spec.window + 1)
+
+
+def make_batch(spec: LayerSpec, ctx_lens, q_lens, key, *, back: str = "visible",
+               shuffle: bool = True, poison: bool = False, extra_pages: int = 0,
+               pt_stride: Optional[int] = None) -> Batch:
+    """Draw one layer's batch.
+
+    back="visible": only pages holding a token some query can see are backed, other
+    page-table entries are -1. back="all": every page up to the row length is backed.
+    poison=True fills never-visible slots (before the first needed token, after the
+    row's end) and ``extra_pages`` unused pages with bf16 NaN.
+    """
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    B = ctx_lens.shape[0]
+    P, Hkv, hd, Hq = spec.page_size, spec.num_kv_heads, spec.head_dim, spec.num_q_heads
+    assert np.all(ctx_lens >= 1) and np.all(q_lens >= 0) and np.all(q_lens <= ctx_lens)
+    need = np.array([first_needed_token(spec, int(L), int(C)) for L, C in zip(ctx_lens, q_lens)], np.int32)
+    k_starts = need if back == "visible" else np.zeros(B, np.int32)
+    first_pg = k_starts // P
+    last_pg = (ctx_lens - 1) // P
+    n_pg = last_pg - first_pg + 1
+    total = int(n_pg.sum())
+    if pt_stride is None:
+        pt_stride = int(((ctx_lens.max() + P - 1) // P)) if B else 1
+    ids = np.arange(total, dtype=np.int64)
+    if shuffle:
+        ids = generator(*key, T_PERM).permutation(total)
+    page_table = np.full((B, pt_stride), -1, dtype=np.int32)
+    pos = 0
+    for r in range(B):
+        page_table[r, first_pg[r]:last_pg[r] + 1] = ids[pos:pos + n_pg[r]]
+        pos += n_pg[r]
+
+    T = int(q_lens.sum())
+    q = normal_bf16(generator(*key, T_Q), (T, Hq, hd))
+    # Draw every slot of every backed page, row after row, then keep the row's stored range.
+    full_tokens = total * P
+    kfull = normal_bf16(generator(*key, T_K), (full_tokens, Hkv, hd))
+    vfull = None if spec.kv_shared else normal_bf16(generator(*key, T_V), (full_tokens, Hkv, hd))
+
+    num_pages = total + extra_pages
+    k_pool = np.empty((num_pages, Hkv, P, hd), dtype=np.uint16)
+    v_pool = None if spec.kv_shared else np.empty_like(k_pool)
+    if extra_pages:
+        k_pool[total:] = BF16_NAN if poison else 0
+        if v_pool is not None:
+            v_pool[total:] = BF16_NAN if poison else 0
+
+    ks, vs = [], []
+    pos_tok = 0
+    for r in range(B):
+        t0 = int(first_pg[r]) * P
+        nt = int(n_pg[r]) * P
+        kr = kfull[pos_tok:pos_tok + nt]
+        vr = None if vfull is None else vfull[pos_tok:pos_tok + nt]
+        pos_tok += nt
+        lo_keep = int(k_starts[r]) - t0
+        hi_keep = int(ctx_lens[r]) - t0
+        ks.append(kr[lo_keep:hi_keep])
+        if vr is not None:
+            vs.append(vr[lo_keep:hi_keep])
+        if poison:
+            kr = kr.copy()
+            kr[:lo_keep] = BF16_NAN
+            kr[hi_keep:] = BF16_NAN
+            if vr is not None:
+                vr = vr.copy()
+                vr[:lo_keep] = BF16_NAN
+                vr[hi_keep:] = BF16_NAN
+        pids = page_table[r, first_pg[r]:last_pg[r] + 1]
+        # token-major rows [n_pg*P][Hkv][hd] -> page-major [n_pg][Hkv][P][hd]
+        k_pool[pids] = kr.reshape(int(n_pg[r]), P, Hkv, hd).transpose(0, 2, 1, 3)
+        if vr is not None:
+            v_pool[pids] = vr.reshape(int(n_pg[r]), P, Hkv, hd).transpose(0, 2, 1, 3)
+    k = np.concatenate(ks) if ks else np.zeros((0, Hkv, hd), np.uint16)
+    v = None if spec.kv_shared else (np.concatenate(vs) if vs else np.zeros((0, Hkv, hd), np.uint16))
+    return Batch(spec, ctx_lens, q_lens, k_starts, q, k, v, page_table, k_pool, v_pool,
+                 {"key": tuple(key), "back": back, "shuffle": shuffle, "poison": poison})
+
+
+def gather_row_from_pool(batch: Batch, r: int, pool: np.ndarray) -> np.ndarray:
+    """Read row r's stored tokens back out of a paged pool (the inverse of the scatter)."""
+    P = batch.spec.page_size
+    t = np.arange(int(batch.k_starts[r]), int(batch.ctx_lens[r]))
+    pids = batch.page_table[r, t // P]
+    return pool[pids, :, t % P, :]
+
+
+# --------------------------------------------------------------------------- configs
+def ragged(key, lo: int, hi: int, n: int) -> np.ndarray:
+    return generator(*key, T_LEN).integers(lo, hi + 1, size=n).astype(np.int32)
+
+
+def cfg1_tiny_decode(**kw) -> Batch:
+    """One row, one local layer (4 q heads, 2 KV heads, hd 256, W 1024), L = 1025, scale 1/16,
+    65 pages taken from a seeded permutation of a 65-page pool."""
+    spec = LayerSpec("local", 4, 2, 256, window=1024, scale=1.0 / 16.0)
+    return make_batch(spec, [1025], [1], (1, 0), back="all", **kw)
+
+
+def cfg2_global_decode(B: int = 32, max_len: int = 8192, **kw) -> Batch:
+    """Global decode: B rows, 32 q heads, 4 KV heads, hd 512, L ~ U{1..max_len}; split 512."""
+    L = ragged((2, 0), 1, max_len, B)
+    return make_batch(GLOBAL_31B, L, np.ones(B, np.int32), (2, 0), back="all", **kw)
+
+
+def cfg3_local_decode(B: int = 64, lo: int = 512, hi: int = 32768, **kw) -> Batch:
+    """Local decode: B rows, 32 q heads, 16 KV heads, hd 256, W 1024, L ~ U{lo..hi}; only
+    window pages are backed."""
+    L = ragged((3, 0), lo, hi, B)
+    return make_batch(LOCAL_31B, L, np.ones(B, np.int32), (3, 0), back="visible", **kw)
+
+
+def cfg4_mixed(family: str, n_prefill: int = 4, chunk: int = 2048, max_prior: int = 6144,
+               n_decode: int = 60, max_decode_len: int = 8192, **kw):
+    """Mixed step: prefill rows (chunk queries after a prior ~ U{0..max_prior}) and decode rows
+    (L ~ U{1..max_decode_len}) of one family. Returns (prefill_batch, decode_batch)."""
+    spec = GLOBAL_31B if family == "global" else LOCAL_31B
+    fam = 1 if family == "global" else 0
+    prior = generator(4, fam, T_PRIOR).integers(0, max_prior + 1, size=n_prefill).astype(np.int32)
+    pre = make_batch(spec, prior + chunk, np.full(n_prefill, chunk, np.int32), (4, fam, 0),
+                     back="visible", **kw)
+    L = ragged((4, fam, 1), 1, max_decode_len, n_decode)
+    dec = make_batch(spec, L, np.ones(n_decode, np.int32), (4, fam, 1), back="visible", **kw)
+    return pre, dec
+
+
+def cfg5_layer_spec(family: str) -> LayerSpec:
+    """Sweep layer geometry: global layers share K and V; local layers are the 31B local family."""
+    return GLOBAL_31B_KV_SHARED if family == "global" else LOCAL_31B
