@@ -55,6 +55,8 @@ def _load():
             lib.oracle_decode_split.restype = c_int
             lib.oracle_decode_split.argtypes = [c_int, c_int, c_int, c_int, c_int, c_double, c_int,
                                                 i32p, i32p, u16p, u16p, u16p, c_int, f64p, f64p]
+            lib.oracle_merge.restype = c_int
+            lib.oracle_merge.argtypes = [ctypes.c_int64, c_int, c_int, f64p, f64p, f64p, f64p]
             lib.oracle_layer_is_global.restype = c_int
             lib.oracle_layer_is_global.argtypes = [c_int, c_int]
             lib.oracle_threads.restype = c_int
@@ -116,6 +118,22 @@ def decode_split(is_global: bool, num_q_heads: int, num_kv_heads: int, head_dim:
                                  _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if rc != OK:
         raise OracleError(f"oracle_decode_split failed: {rc}")
+    return out, lse
+
+
+def merge(lse_parts, o_parts):
+    """Logsumexp merge in fp64. lse_parts [..., n]; o_parts [..., n, hd] -> (out [..., hd], lse [...])."""
+    lib = _load()
+    lp = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    op = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lead, n, hd = lp.shape[:-1], lp.shape[-1], op.shape[-1]
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.empty(lead + (hd,), dtype=np.float64)
+    lse = np.empty(lead, dtype=np.float64)
+    rc = lib.oracle_merge(rows, n, hd, _ptr(lp, ctypes.c_double), _ptr(op, ctypes.c_double),
+                          _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != OK:
+        raise OracleError(f"oracle_merge failed: {rc}")
     return out, lse
 
 

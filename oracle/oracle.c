@@ -204,6 +204,46 @@ int oracle_attend(int is_global, int Hq, int Hkv, int hd, int window, double sca
     return failed ? ORACLE_NO_MEM : ORACLE_OK;
 }
 
+/* Merge pieces by logsumexp: M = max lse_i, LSE = M + ln sum_i exp(lse_i - M),
+ * O = sum_i exp(lse_i - LSE) o_i. Pieces with lse = -inf are empty and skipped; with no
+ * non-empty piece O = 0 and LSE = -inf. Returns LSE. */
+static double merge_parts(int np, int hd, const double *lse_parts, const double *o_parts, double *o)
+{
+    double M = -INFINITY;
+    for (int i = 0; i < np; ++i)
+        if (lse_parts[i] > M)
+            M = lse_parts[i];
+    for (int d = 0; d < hd; ++d)
+        o[d] = 0.0;
+    if (M == -INFINITY)
+        return -INFINITY;
+    double sum = 0.0;
+    for (int i = 0; i < np; ++i)
+        if (lse_parts[i] != -INFINITY)
+            sum += exp(lse_parts[i] - M);
+    double L = M + log(sum);
+    for (int i = 0; i < np; ++i) {
+        if (lse_parts[i] == -INFINITY)
+            continue;
+        double w = exp(lse_parts[i] - L);
+        for (int d = 0; d < hd; ++d)
+            o[d] += w * o_parts[i * (int64_t)hd + d];
+    }
+    return L;
+}
+
+int oracle_merge(int64_t n_rows, int n_parts, int hd, const double *lse_parts, const double *o_parts,
+                 double *out, double *lse)
+{
+    if (n_rows < 0 || n_parts < 1 || hd < 1)
+        return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r)
+        lse[r] = merge_parts(n_parts, hd, lse_parts + r * n_parts, o_parts + r * n_parts * (int64_t)hd,
+                             out + r * (int64_t)hd);
+    return ORACLE_OK;
+}
+
 int oracle_decode_split(int is_global, int Hq, int Hkv, int hd, int window, double scale,
                         int B, const int32_t *ctx_lens, const int32_t *k_starts,
                         const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -263,24 +303,7 @@ int oracle_decode_split(int is_global, int Hq, int Hkv, int hd, int window, doub
                     lse_parts[np] = attend_range(&pb, r, kv, qv, a, b, scores, o_parts + np * (int64_t)hd);
                     ++np;
                 }
-                /* merge by logsumexp */
-                double M = -INFINITY;
-                for (int i = 0; i < np; ++i)
-                    if (lse_parts[i] > M)
-                        M = lse_parts[i];
-                double sum = 0.0;
-                for (int i = 0; i < np; ++i)
-                    sum += exp(lse_parts[i] - M);
-                double L = M + log(sum);
-                double *o = out + item * (int64_t)hd;
-                for (int d = 0; d < hd; ++d)
-                    o[d] = 0.0;
-                for (int i = 0; i < np; ++i) {
-                    double w = exp(lse_parts[i] - L);
-                    for (int d = 0; d < hd; ++d)
-                        o[d] += w * o_parts[i * (int64_t)hd + d];
-                }
-                lse[item] = L;
+                lse[item] = merge_parts(np, hd, lse_parts, o_parts, out + item * (int64_t)hd);
             }
         }
         free(scores);

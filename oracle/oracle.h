@@ -36,6 +36,11 @@ int oracle_decode_split(int is_global, int Hq, int Hkv, int hd, int window, doub
                         const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int split_tokens, double *out, double *lse);
 
+/* Logsumexp merge of n_parts pieces per row (empty pieces have lse = -inf).
+ * lse_parts: [n_rows][n_parts]; o_parts: [n_rows][n_parts][hd]; out: [n_rows][hd]; lse: [n_rows]. */
+int oracle_merge(int64_t n_rows, int n_parts, int hd, const double *lse_parts, const double *o_parts,
+                 double *out, double *lse);
+
 /* 1 if layer is global, 0 if local, -1 if n_layers is not a whole number of
  * five-local-one-global groups (the stack must end on a global layer). */
 int oracle_layer_is_global(int layer, int n_layers);

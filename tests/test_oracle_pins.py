@@ -256,6 +256,30 @@ def test_p7_split_merge_equals_unsplit(fam, W, S):
     assert np.max(np.abs(o - os_)) < 1e-12 and np.max(np.abs(l - ls)) < 1e-12
 
 
+def test_p7_standalone_merge_of_disjoint_pieces():
+    """Pieces attended separately (each normalised, with its own LSE) merge to the whole row, and
+    empty pieces (lse = -inf) are ignored, whatever their o holds."""
+    Hq, Hkv, hd, L = 2, 1, 8, 40
+    q, k, v = _tiny_case((24,), L, Hq, Hkv, hd)
+    whole_o, whole_l = oracle.attend(True, Hq, Hkv, hd, 0, 0.5, [1], [L], None, q[-1:], k, v)
+    cuts = [0, 7, 8, 23, 40]
+    lps, ops = [], []
+    for a, e in zip(cuts[:-1], cuts[1:]):
+        # attend keys [a, e) from the final query: a local window ending at e - 1 starting at a
+        qq = q[-1:]
+        o, l = oracle.attend(False, Hq, Hkv, hd, e - a, 0.5, [1], [e], [a], qq, k[a:e], v[a:e])
+        lps.append(l[0])
+        ops.append(o[0])
+    lps.append(np.full(Hq, -np.inf))
+    ops.append(np.full((Hq, hd), np.nan))
+    lp = np.stack(lps, axis=1)            # [Hq][n]
+    op = np.stack(ops, axis=1)            # [Hq][n][hd]
+    mo, ml = oracle.merge(lp, np.nan_to_num(op, nan=1e300))
+    assert np.max(np.abs(mo - whole_o[0])) < 1e-12 and np.max(np.abs(ml - whole_l[0])) < 1e-12
+    eo, el = oracle.merge(np.full((1, 3), -np.inf), np.zeros((1, 3, 4)))
+    assert el[0] == -np.inf and np.all(eo == 0)
+
+
 # ---------------------------------------------------------------- P8: chunk parity (G5)
 @pytest.mark.parametrize("fam,W", [("global", 0), ("local", 64)])
 def test_p8_chunks_equal_token_by_token(fam, W):
