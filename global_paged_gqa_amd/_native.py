@@ -1,0 +1,139 @@
+"""ctypes binding of libgattn.so: the C ABI of include/gattn.h under the same names.
+
+Argument marshalling only: pointers may be torch tensors (their data_ptr()),
+numpy arrays (host pointers, for gattn_kv_offset), raw integer addresses or
+None. Every computation happens in the library's HIP kernels. A nonzero status
+raises GattnError carrying the status code.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build the gfx950 library first "
+                      "(python -c 'import __graft_entry__ as g; g.build()')")
+_lib = ctypes.CDLL(LIB_PATH)
+
+LOCAL, GLOBAL = 0, 1
+OK, ERR_NULL_PTR, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_BAD_SPLIT, ERR_HIP = range(7)
+PAGE_SIZE = 16
+
+c_int, c_i64, c_size, c_vp, c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+class Layer(ctypes.Structure):
+    """struct gattn_layer."""
+    _fields_ = [("family", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("kv_shared", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def make_layer(family, num_q_heads, num_kv_heads, head_dim, window=0, kv_shared=False, scale=None,
+               page_size=PAGE_SIZE):
+    fam = family if isinstance(family, int) else (GLOBAL if family == "global" else LOCAL)
+    if scale is None:
+        scale = head_dim ** -0.5
+    return Layer(fam, num_q_heads, num_kv_heads, head_dim, window, page_size, int(bool(kv_shared)), scale)
+
+
+class GattnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {gattn_status_str(status)} (status {status})")
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+
+
+_lib.gattn_abi_version.restype = c_int
+_lib.gattn_abi_version.argtypes = []
+_lib.gattn_status_str.restype = ctypes.c_char_p
+_lib.gattn_status_str.argtypes = [c_int]
+_lib.gattn_layer_family.restype = c_int
+_lib.gattn_layer_family.argtypes = [c_int, c_int]
+_lib.gattn_kv_offset.restype = c_i64
+_lib.gattn_kv_offset.argtypes = [ctypes.POINTER(Layer), c_vp, c_int, c_int, c_int, c_int, c_int, c_i64]
+_lib.gattn_decode_workspace_bytes.restype = c_size
+_lib.gattn_decode_workspace_bytes.argtypes = [ctypes.POINTER(Layer), c_int, c_int, c_int]
+_lib.gattn_decode.restype = c_int
+_lib.gattn_decode.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_int, c_int,
+                              c_int, c_vp, c_size, c_vp, c_vp, c_vp]
+_lib.gattn_prefill.restype = c_int
+_lib.gattn_prefill.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_vp, c_int,
+                               c_int, c_vp, c_vp, c_vp]
+_lib.gattn_combine.restype = c_int
+_lib.gattn_combine.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]
+
+
+def _check(rc, where):
+    if rc != OK:
+        raise GattnError(rc, where)
+
+
+def gattn_abi_version():
+    return _lib.gattn_abi_version()
+
+
+def gattn_status_str(status):
+    return _lib.gattn_status_str(int(status)).decode()
+
+
+def gattn_layer_family(layer, n_layers):
+    return _lib.gattn_layer_family(int(layer), int(n_layers))
+
+
+def gattn_kv_offset(layer, page_table_host, rows, pt_stride, row, token, kv_head, num_pages):
+    return _lib.gattn_kv_offset(ctypes.byref(layer), _addr(page_table_host), rows, pt_stride, row, token,
+                                kv_head, num_pages)
+
+
+def gattn_decode_workspace_bytes(layer, batch, max_ctx, split_tokens):
+    return _lib.gattn_decode_workspace_bytes(ctypes.byref(layer), batch, max_ctx, split_tokens)
+
+
+def gattn_decode(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, ctx_lens, batch, max_ctx,
+                 split_tokens, workspace, workspace_bytes, out, lse, stream=None):
+    rc = _lib.gattn_decode(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), int(num_pages),
+                           _addr(page_table), int(pt_stride), _addr(ctx_lens), int(batch), int(max_ctx),
+                           int(split_tokens), _addr(workspace), int(workspace_bytes), _addr(out), _addr(lse),
+                           _stream(stream))
+    _check(rc, "gattn_decode")
+
+
+def gattn_prefill(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, cu_q, ctx_lens, batch, max_q,
+                  out, lse, stream=None):
+    rc = _lib.gattn_prefill(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), int(num_pages),
+                            _addr(page_table), int(pt_stride), _addr(cu_q), _addr(ctx_lens), int(batch),
+                            int(max_q), _addr(out), _addr(lse), _stream(stream))
+    _check(rc, "gattn_prefill")
+
+
+def gattn_combine(batch, num_q_heads, head_dim, num_splits, o_part, lse_part, out, lse, stream=None):
+    rc = _lib.gattn_combine(int(batch), int(num_q_heads), int(head_dim), int(num_splits), _addr(o_part),
+                            _addr(lse_part), _addr(out), _addr(lse), _stream(stream))
+    _check(rc, "gattn_combine")
+
+
+def exported_symbols():
+    """Names the shared library exports (for the ABI check)."""
+    return sorted(n for n in ("gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
+                              "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine")
+                  if hasattr(_lib, n))

@@ -1,0 +1,55 @@
+// Internal launch interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gattn {
+
+struct DecodeArgs {
+    const uint16_t *q;
+    const uint16_t *k_pool;
+    const uint16_t *v_pool;
+    const int32_t *page_table;
+    const int32_t *ctx_lens;
+    float *o_part;     // per-split partials (several splits per row)
+    float *lse_part;
+    uint16_t *out;     // final outputs (one split per row)
+    float *lse;
+    int64_t num_pages;
+    int pt_stride;
+    int num_q_heads, num_kv_heads, group;
+    int is_global, window;
+    int split_tokens;  // keys per split
+    int n_slots;       // splits per row the grid covers
+    int max_ctx;
+    float scale_log2;  // softmax scale times log2(e)
+};
+
+struct PrefillArgs {
+    const uint16_t *q;
+    const uint16_t *k_pool;
+    const uint16_t *v_pool;
+    const int32_t *page_table;
+    const int32_t *cu_q;
+    const int32_t *ctx_lens;
+    uint16_t *out;
+    float *lse;
+    int64_t num_pages;
+    int pt_stride;
+    int num_q_heads, num_kv_heads, group;
+    int is_global, window;
+    int max_q;
+    float scale_log2;
+};
+
+hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
+                               hipStream_t stream);
+
+hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
+                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillArgs &a, int head_dim, bool kv_shared, int batch,
+                          hipStream_t stream);
+
+}  // namespace gattn

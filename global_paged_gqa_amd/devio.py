@@ -1,0 +1,87 @@
+"""Device-side convenience around the C ABI for tests and the benchmark.
+
+Moves a workloads.Batch (numpy, bf16 bit patterns) into torch device tensors and
+calls gattn_decode / gattn_prefill through the binding. Argument marshalling
+only: no attention arithmetic happens here.
+"""
+import numpy as np
+import torch
+
+from . import _native as nat
+
+
+def dev(a, dtype=None):
+    """numpy -> cuda tensor; uint16 (bf16 bits) travels as int16 with the same bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def host_bf16(t):
+    """cuda int16 tensor of bf16 bits -> numpy float32."""
+    u = t.detach().cpu().numpy().view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+def layer_of(spec):
+    return nat.make_layer(spec.family, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.window,
+                          spec.kv_shared, spec.softmax_scale)
+
+
+class DeviceBatch:
+    """A Batch's paged side resident on the GPU."""
+
+    def __init__(self, batch):
+        self.batch = batch
+        s = batch.spec
+        self.layer = layer_of(s)
+        self.q = dev(batch.q)
+        self.k_pool = dev(batch.k_pool)
+        self.v_pool = None if batch.v_pool is None else dev(batch.v_pool)
+        self.page_table = dev(batch.page_table.astype(np.int32))
+        self.ctx_lens = dev(batch.ctx_lens.astype(np.int32))
+        self.cu_q = dev(batch.cu_q.astype(np.int32))
+        self.num_pages = batch.num_pages
+        self.pt_stride = batch.pt_stride
+        T = int(batch.q_lens.sum())
+        self.out = torch.empty((T, s.num_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+        self.lse = torch.empty((T, s.num_q_heads), dtype=torch.float32, device="cuda")
+        self.workspace = None
+        self.ws_bytes = 0
+
+    def decode(self, split_tokens, max_ctx=None, stream=None, poison_workspace=True):
+        b = self.batch
+        B = b.B
+        max_ctx = int(b.ctx_lens.max()) if max_ctx is None else int(max_ctx)
+        need = nat.gattn_decode_workspace_bytes(self.layer, B, max_ctx, split_tokens)
+        if need > self.ws_bytes:
+            self.workspace = torch.empty(need // 4, dtype=torch.float32, device="cuda")
+            self.ws_bytes = need
+            if poison_workspace:
+                self.workspace.fill_(float("nan"))
+        nat.gattn_decode(self.layer, self.q, self.k_pool, self.v_pool, self.num_pages, self.page_table,
+                         self.pt_stride, self.ctx_lens, B, max_ctx, split_tokens, self.workspace, self.ws_bytes,
+                         self.out, self.lse, stream)
+
+    def prefill(self, max_q=None, stream=None):
+        b = self.batch
+        max_q = int(b.q_lens.max()) if max_q is None else int(max_q)
+        nat.gattn_prefill(self.layer, self.q, self.k_pool, self.v_pool, self.num_pages, self.page_table,
+                          self.pt_stride, self.cu_q, self.ctx_lens, b.B, max_q, self.out, self.lse, stream)
+
+    def result(self):
+        torch.cuda.synchronize()
+        return host_bf16(self.out).astype(np.float64), self.lse.cpu().numpy().astype(np.float64)
+
+
+def decode(batch, split_tokens, max_ctx=None):
+    d = DeviceBatch(batch)
+    d.decode(split_tokens, max_ctx)
+    return d.result()
+
+
+def prefill(batch, max_q=None):
+    d = DeviceBatch(batch)
+    d.prefill(max_q)
+    return d.result()

@@ -1,0 +1,199 @@
+/*
+ * gattn.h -- hybrid paged GQA attention for AMD Instinct MI355X (gfx950): public C ABI.
+ *
+ * What the library computes. Gemma-4-style attention for one layer over a paged
+ * KV cache, for two layer families (pegainfer issue "[Model] Gemma 4 M1 12B",
+ * Description):
+ *   - local:  sliding-window attention; a query at position p sees keys
+ *             max(0, p - window + 1) .. p (the last `window` positions, itself
+ *             included); head_dim 256 and a 1024-token window in Gemma 4 31B;
+ *   - global: full causal attention (keys 0 .. p); head_dim 512 with fewer KV
+ *             heads (4 against 32 query heads at 31B, Core AI card, section
+ *             "hybrid-pf64/ bundles"), optionally with V read from the K cache
+ *             ("K and V projection sharing", same Description).
+ * Query head h reads KV head floor(h / (num_q_heads / num_kv_heads)) (the
+ * block-GQA mapping named in the hybrid-pf64 numerics-gate paragraph). For every
+ * (query, query head) the library returns the softmax-weighted sum of V and the
+ * natural-log logsumexp of the scaled scores:
+ *   s_j = scale * q . k_j,  LSE = ln sum_j exp(s_j),  O = sum_j exp(s_j - LSE) v_j.
+ *
+ * Data types. bf16 arrays are passed as uint16_t bit patterns (bfloat16,
+ * round-to-nearest-even when the library produces them). LSE and split partials
+ * are fp32. All arithmetic on the device accumulates in fp32.
+ *
+ * KV pool layout (one pool per layer; K and V have separate pools unless shared):
+ *   pool[num_pages][num_kv_heads][page_size][head_dim] bf16, page_size = 16.
+ *   Token t of row r lives in page page_table[r * pt_stride + t / 16], slot
+ *   t % 16; its (kv_head, d) element sits at element offset
+ *   ((page * num_kv_heads + kv_head) * 16 + t % 16) * head_dim + d.
+ *   gattn_kv_offset() is the one checked helper that computes this offset (the
+ *   pegainfer "[Model] Gemma 4 M2 26B-A4B" plan routes hand-derived page offsets
+ *   through a checked helper). A page-table entry is read only if its page holds
+ *   a token the call reads; other entries may hold anything, -1 included.
+ *
+ * Ownership. The caller allocates every buffer (device memory unless noted) and
+ * keeps it alive until the work on `stream` has finished. The library never
+ * allocates, frees or synchronises, keeps no mutable global state, and is safe
+ * to call from several host threads. `stream` is a hipStream_t (NULL = the
+ * default stream); every call only enqueues work on it.
+ *
+ * Errors. Argument errors are detected on the host before anything is enqueued
+ * and returned as a gattn_status; the call then has no effect. A failed kernel
+ * launch returns GATTN_ERR_HIP. Inconsistent data that only the device can see
+ * (a context length outside [1, max_ctx] or beyond the page table, a page id
+ * outside [0, num_pages) for a page that holds a visible token) never faults:
+ * the affected row's outputs are written as NaN (fail closed). No C++
+ * exception crosses this interface.
+ */
+#ifndef GATTN_H
+#define GATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GATTN_ABI_VERSION 1
+#define GATTN_PAGE_SIZE 16
+
+enum gattn_family { GATTN_LOCAL = 0, GATTN_GLOBAL = 1 };
+
+enum gattn_status {
+    GATTN_OK = 0,
+    GATTN_ERR_NULL_PTR = 1,             /* a required pointer is NULL */
+    GATTN_ERR_BAD_SHAPE = 2,            /* negative or inconsistent sizes */
+    GATTN_ERR_UNSUPPORTED = 3,          /* valid but not served: head_dim, page size, group size, ... */
+    GATTN_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes < gattn_decode_workspace_bytes() */
+    GATTN_ERR_BAD_SPLIT = 5,            /* split_tokens not 0 and not a positive multiple of 16 */
+    GATTN_ERR_HIP = 6                   /* a HIP launch failed */
+};
+
+/*
+ * One layer's geometry. Served: head_dim 256 or 512; page_size 16;
+ * num_q_heads a multiple of num_kv_heads with group num_q_heads/num_kv_heads
+ * between 1 and 16; local layers need window >= 1 (global layers ignore it);
+ * kv_shared 0 or 1; scale finite (Gemma 4 uses 1.0; 1/sqrt(head_dim) is the
+ * textbook value). Anything else returns GATTN_ERR_UNSUPPORTED or BAD_SHAPE.
+ */
+typedef struct gattn_layer {
+    int32_t family;        /* GATTN_LOCAL or GATTN_GLOBAL */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t window;        /* local: keys visible to a query, itself included */
+    int32_t page_size;     /* must be 16 */
+    int32_t kv_shared;     /* 1: V is read from the K pool (v_pool must equal k_pool) */
+    float scale;           /* multiplies q . k before the softmax */
+} gattn_layer;
+
+/* Library ABI version (GATTN_ABI_VERSION of the build). */
+int gattn_abi_version(void);
+
+/* Static text for a gattn_status value. */
+const char *gattn_status_str(int status);
+
+/*
+ * Layer schedule of a Gemma 4 decoder stack: five local layers then one global
+ * layer, repeated, so that the last layer is global (pegainfer "[Model] Gemma 4
+ * M3 31B", Description and Acceptance Criteria: 60 layers, five-to-one pattern,
+ * final-global-layer assertion). Returns GATTN_LOCAL or GATTN_GLOBAL, or -1 if
+ * layer is outside [0, n_layers) or n_layers is not a positive multiple of 6.
+ */
+int gattn_layer_family(int layer, int n_layers);
+
+/*
+ * The checked page-offset helper. Host-only: page_table_host is host memory,
+ * [rows][pt_stride] int32. Returns the element offset of element 0 of
+ * (row, token, kv_head) in a pool of num_pages pages, or -1 if any index is out
+ * of range (row, token beyond the table, kv_head, or a page id outside
+ * [0, num_pages)).
+ */
+int64_t gattn_kv_offset(const gattn_layer *layer, const int32_t *page_table_host, int rows,
+                        int pt_stride, int row, int token, int kv_head, int64_t num_pages);
+
+/*
+ * Split-KV decode workspace size in bytes for a call with these arguments, or 0
+ * if the arguments are invalid. The workspace holds per-split partials
+ * (fp32 o[batch][num_q_heads][slots][head_dim] followed by fp32
+ * lse[batch][num_q_heads][slots]). When a call needs a single split per row the
+ * size is 0 bytes and the workspace pointer may be NULL: the split kernel then
+ * writes the outputs itself. The size depends only on the arguments, so a
+ * caller can allocate it once for its largest call (fixed-capacity scratch, as
+ * the pegainfer "[Model] Gemma 4 M2 26B-A4B" description asks for graph-safe
+ * use).
+ */
+size_t gattn_decode_workspace_bytes(const gattn_layer *layer, int batch, int max_ctx, int split_tokens);
+
+/*
+ * Single-token decode with split-KV flash-decoding and a logsumexp combine
+ * (pegainfer "[Model] Gemma 4 M3 31B", Proposed Plan: decode graph buckets and
+ * split-KV chunk policy; Core AI card, "--metal-sdpa" section: flash-decode
+ * kernel with a split factor).
+ *
+ *   q          [batch][num_q_heads][head_dim] bf16: one query per row, at
+ *              position ctx_lens[r] - 1.
+ *   k_pool     KV pool (layout above); v_pool likewise, or equal to k_pool when
+ *              layer->kv_shared (then V is never read separately).
+ *   num_pages  pages in each pool (bounds every page id the device reads).
+ *   page_table [batch][pt_stride] int32 (device memory).
+ *   ctx_lens   [batch] int32 (device memory): tokens in the cache including the
+ *              current one; must be in [1, max_ctx] and fit the page table.
+ *   max_ctx    host-side upper bound of ctx_lens; sets the grid, so the call
+ *              enqueues the same work for any ctx_lens (HIP-graph capturable).
+ *   split_tokens  keys per split, a positive multiple of 16, or 0 for one
+ *              split per row. Split boundaries are absolute multiples of
+ *              split_tokens from token 0, so results do not depend on the batch.
+ *   workspace  at least gattn_decode_workspace_bytes(...) bytes (may be NULL if
+ *              that is 0).
+ *   out        [batch][num_q_heads][head_dim] bf16.
+ *   lse        [batch][num_q_heads] fp32, natural log.
+ * Enqueues the split kernel, then (when a row can have several splits) the
+ * combine kernel, on `stream`.
+ */
+int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
+                 const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                 const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
+                 size_t workspace_bytes, uint16_t *out, float *lse, void *stream);
+
+/*
+ * Chunked causal prefill (Core AI card, "Contents": a flash-prefill with a
+ * query axis and an intra-chunk causal mask; "hybrid-pf64/ bundles": a prefill
+ * entrypoint next to decode). Row r has q_len = cu_q[r+1] - cu_q[r] queries at
+ * absolute positions ctx_lens[r] - q_len + i; the chunk's own K/V are already in
+ * the pool. Rows with q_len 0 are skipped; q_len 1 rows are legal (a mixed
+ * step may send decode rows here).
+ *
+ *   q          [total_q][num_q_heads][head_dim] bf16, rows back to back.
+ *   cu_q       [batch + 1] int32 (device memory), cu_q[0] = 0, nondecreasing.
+ *   ctx_lens   [batch] int32 (device memory), ctx_lens[r] >= q_len of row r.
+ *   max_q      host-side upper bound of every row's q_len (sets the grid).
+ *   out        [total_q][num_q_heads][head_dim] bf16.
+ *   lse        [total_q][num_q_heads] fp32, natural log.
+ */
+int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
+                  const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                  const int32_t *cu_q, const int32_t *ctx_lens, int batch, int max_q, uint16_t *out,
+                  float *lse, void *stream);
+
+/*
+ * Logsumexp merge of split partials (the combine half of split-KV decoding).
+ * For each (row, head): M = max over splits of lse_s; LSE = M + ln sum_s
+ * exp(lse_s - M); O = sum_s exp(lse_s - LSE) o_s. Splits with lse_s = -inf are
+ * empty and are skipped (their o_s is never read). A row whose splits are all
+ * empty gets O = 0 and LSE = -inf.
+ *
+ *   o_part     [batch][num_q_heads][num_splits][head_dim] fp32, each split's
+ *              output already normalised by its own softmax sum.
+ *   lse_part   [batch][num_q_heads][num_splits] fp32.
+ *   out        [batch][num_q_heads][head_dim] bf16; lse [batch][num_q_heads] fp32.
+ * head_dim must be a positive multiple of 4 and at most 1024.
+ */
+int gattn_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
+                  const float *lse_part, uint16_t *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GATTN_H */

@@ -1,0 +1,164 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point, and
+rejects bad arguments with the documented status before touching the device."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+
+import global_paged_gqa_amd as g  # noqa: E402
+from global_paged_gqa_amd import _native as nat  # noqa: E402
+import workloads  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gattn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
+                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine"])
+    for n in names:
+        assert hasattr(nat._lib, n), n
+    assert g.gattn_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(7):
+        assert g.gattn_status_str(s) and g.gattn_status_str(s) != "unknown status"
+    assert g.gattn_status_str(99) == "unknown status"
+
+
+def test_layer_family_schedule():
+    fam = [g.gattn_layer_family(l, 60) for l in range(60)]
+    assert fam.count(g.GLOBAL) == 10 and fam.count(g.LOCAL) == 50 and fam[59] == g.GLOBAL
+    assert fam[:6] == [0, 0, 0, 0, 0, 1]
+    assert g.gattn_layer_family(0, 59) == -1 and g.gattn_layer_family(60, 60) == -1
+    assert g.gattn_layer_family(-1, 60) == -1
+
+
+def test_kv_offset_hand_computed():
+    lay = g.make_layer("global", 32, 4, 512)
+    pt = np.array([[5, 2, -1, 7], [0, 1, 3, 6]], dtype=np.int32)
+    cases = [  # (row, token, kv_head, expected)
+        (0, 0, 0, ((5 * 4 + 0) * 16 + 0) * 512),
+        (0, 15, 3, ((5 * 4 + 3) * 16 + 15) * 512),
+        (0, 16, 1, ((2 * 4 + 1) * 16 + 0) * 512),
+        (0, 31, 2, ((2 * 4 + 2) * 16 + 15) * 512),
+        (0, 48, 0, ((7 * 4 + 0) * 16 + 0) * 512),
+        (1, 0, 0, 0),
+        (1, 17, 2, ((1 * 4 + 2) * 16 + 1) * 512),
+        (1, 63, 3, ((6 * 4 + 3) * 16 + 15) * 512),
+        (0, 32, 0, -1),      # page -1
+        (0, 64, 0, -1),      # beyond the table
+        (2, 0, 0, -1),       # row out of range
+        (1, 0, 4, -1),       # kv head out of range
+        (1, 40, 0, -1),      # page 3 >= num_pages 3
+    ]
+    for row, tok, kvh, want in cases:
+        assert g.gattn_kv_offset(lay, pt, 2, 4, row, tok, kvh, 8 if want != -1 or row != 1 else 3) == want, \
+            (row, tok, kvh)
+    loc = g.make_layer("local", 32, 16, 256, window=1024)
+    assert g.gattn_kv_offset(loc, pt, 2, 4, 1, 35, 9, 8) == ((3 * 16 + 9) * 16 + 3) * 256
+
+
+def test_kv_offset_agrees_with_the_scatter():
+    """The checked helper and the independent scatter in workloads agree on every stored token."""
+    b = workloads.cfg1_tiny_decode()
+    lay = g.make_layer("local", 4, 2, 256, 1024, scale=1 / 16)
+    flat = b.k_pool.reshape(-1)
+    for tok in (0, 1, 15, 16, 511, 1000, 1024):
+        for kvh in (0, 1):
+            off = g.gattn_kv_offset(lay, b.page_table, 1, b.pt_stride, 0, tok, kvh, b.num_pages)
+            assert np.array_equal(flat[off:off + 256], b.k[tok, kvh])
+
+
+def test_workspace_bytes():
+    glob = g.make_layer("global", 32, 4, 512)
+    assert g.gattn_decode_workspace_bytes(glob, 32, 8192, 512) == 32 * 32 * 16 * 513 * 4
+    assert g.gattn_decode_workspace_bytes(glob, 32, 8192, 0) == 0          # one split per row
+    assert g.gattn_decode_workspace_bytes(glob, 32, 512, 512) == 0
+    assert g.gattn_decode_workspace_bytes(glob, 1, 65536, 1024) == 32 * 64 * 513 * 4
+    loc = g.make_layer("local", 32, 16, 256, window=1024)
+    # a 1024-key window touches at most 3 splits of 512 and 2 of 1024, whatever the context
+    assert g.gattn_decode_workspace_bytes(loc, 64, 32768, 512) == 64 * 32 * 3 * 257 * 4
+    assert g.gattn_decode_workspace_bytes(loc, 64, 32768, 1024) == 64 * 32 * 2 * 257 * 4
+    assert g.gattn_decode_workspace_bytes(loc, 64, 32768, 16) == 64 * 32 * 65 * 257 * 4
+    assert g.gattn_decode_workspace_bytes(glob, 32, 8192, 500) == 0        # bad split
+    assert g.gattn_decode_workspace_bytes(glob, 32, 0, 512) == 0
+
+
+def _decode_status(**over):
+    lay = over.pop("layer", g.make_layer("global", 32, 4, 512))
+    args = dict(q=1 << 20, k_pool=2 << 20, v_pool=3 << 20, num_pages=100, page_table=4 << 20, pt_stride=512,
+                ctx_lens=5 << 20, batch=32, max_ctx=8192, split_tokens=512, workspace=6 << 20,
+                workspace_bytes=1 << 30, out=7 << 20, lse=8 << 20)
+    args.update(over)
+    try:
+        g.gattn_decode(lay, **args, stream=0)
+    except g.GattnError as e:
+        return e.status
+    return 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), nat.ERR_NULL_PTR),
+    (dict(k_pool=None), nat.ERR_NULL_PTR),
+    (dict(v_pool=None), nat.ERR_NULL_PTR),
+    (dict(page_table=None), nat.ERR_NULL_PTR),
+    (dict(ctx_lens=None), nat.ERR_NULL_PTR),
+    (dict(out=None), nat.ERR_NULL_PTR),
+    (dict(lse=None), nat.ERR_NULL_PTR),
+    (dict(workspace=None), nat.ERR_NULL_PTR),
+    (dict(batch=-1), nat.ERR_BAD_SHAPE),
+    (dict(max_ctx=0), nat.ERR_BAD_SHAPE),
+    (dict(pt_stride=0), nat.ERR_BAD_SHAPE),
+    (dict(pt_stride=511), nat.ERR_BAD_SHAPE),       # table cannot hold max_ctx tokens
+    (dict(num_pages=0), nat.ERR_BAD_SHAPE),
+    (dict(split_tokens=500), nat.ERR_BAD_SPLIT),
+    (dict(split_tokens=-16), nat.ERR_BAD_SPLIT),
+    (dict(workspace_bytes=100), nat.ERR_WORKSPACE_TOO_SMALL),
+    (dict(layer=g.make_layer("global", 32, 4, 128)), nat.ERR_UNSUPPORTED),
+    (dict(layer=g.make_layer("global", 32, 4, 512, page_size=32)), nat.ERR_UNSUPPORTED),
+    (dict(layer=g.make_layer("global", 32, 5, 512)), nat.ERR_BAD_SHAPE),
+    (dict(layer=g.make_layer("global", 64, 2, 512)), nat.ERR_UNSUPPORTED),   # group 32 > 16
+    (dict(layer=g.make_layer("local", 32, 16, 256, window=0)), nat.ERR_BAD_SHAPE),
+    (dict(layer=g.make_layer("global", 32, 4, 512, scale=math.inf)), nat.ERR_BAD_SHAPE),
+    (dict(layer=g.make_layer(7, 32, 4, 512)), nat.ERR_UNSUPPORTED),
+    (dict(layer=g.make_layer("global", 32, 4, 512, kv_shared=True)), nat.ERR_BAD_SHAPE),  # v_pool != k_pool
+    (dict(batch=0), 0),
+])
+def test_decode_rejects_bad_arguments_without_a_device(over, status):
+    assert _decode_status(**over) == status
+    assert _decode_status(batch=0) == 0  # no sticky state after a rejected call
+
+
+def test_prefill_and_combine_reject_bad_arguments():
+    lay = g.make_layer("local", 32, 16, 256, window=1024)
+    ok = dict(q=1, k_pool=2, v_pool=3, num_pages=10, page_table=4, pt_stride=8, cu_q=5, ctx_lens=6, batch=0,
+              max_q=16, out=7, lse=8)
+
+    def st(fn, *a, **kw):
+        try:
+            fn(*a, **kw, stream=0)
+        except g.GattnError as e:
+            return e.status
+        return 0
+    assert st(g.gattn_prefill, lay, **ok) == 0
+    assert st(g.gattn_prefill, lay, **dict(ok, cu_q=None)) == nat.ERR_NULL_PTR
+    assert st(g.gattn_prefill, lay, **dict(ok, max_q=-1)) == nat.ERR_BAD_SHAPE
+    assert st(g.gattn_prefill, g.make_layer("local", 32, 16, 256, window=-5), **ok) == nat.ERR_BAD_SHAPE
+    assert st(g.gattn_combine, 4, 32, 512, 0, 1, 2, 3, 4) == nat.ERR_BAD_SHAPE
+    assert st(g.gattn_combine, 4, 32, 510, 3, 1, 2, 3, 4) == nat.ERR_UNSUPPORTED
+    assert st(g.gattn_combine, 4, 32, 512, 3, None, 2, 3, 4) == nat.ERR_NULL_PTR
+    assert st(g.gattn_combine, 0, 32, 512, 3, 1, 2, 3, 4) == 0

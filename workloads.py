@@ -290,3 +290,22 @@ def cfg4_mixed(family: str, n_prefill: int = 4, chunk: int = 2048, max_prior: in
 def cfg5_layer_spec(family: str) -> LayerSpec:
     """Sweep layer geometry: global layers share K and V; local layers are the 31B local family."""
     return GLOBAL_31B_KV_SHARED if family == "global" else LOCAL_31B
+
+
+def permute_pages(batch: Batch, key, extra_pages: int = 0, fill=0) -> Batch:
+    """Same rows and values, different physical pages: a seeded relabelling of every page
+    id (plus ``extra_pages`` unused pages filled with ``fill`` bits)."""
+    n = batch.num_pages
+    perm = generator(*key, T_PERM).permutation(n + extra_pages)[:n]
+    k_pool = np.full((n + extra_pages,) + batch.k_pool.shape[1:], fill, dtype=np.uint16)
+    k_pool[perm] = batch.k_pool
+    v_pool = None
+    if batch.v_pool is not None:
+        v_pool = np.full_like(k_pool, fill)
+        v_pool[perm] = batch.v_pool
+    pt = batch.page_table.copy()
+    m = pt >= 0
+    pt[m] = perm[pt[m]]
+    out = replace(batch, page_table=pt, k_pool=k_pool, v_pool=v_pool)
+    out.meta = dict(batch.meta, repaged=tuple(key))
+    return out
