@@ -1,0 +1,237 @@
+"""Benchmark of the hybrid paged GQA attention hot path on one MI355X.
+
+Workload (the metric's configuration): global-family split-KV decode, batch 32,
+32 query heads, 4 KV heads, head_dim 512, ragged contexts ~ U{1..8192}, page
+size 16, globally shuffled page tables, 512-token splits, bf16 N(0,1) inputs.
+One step = one gattn_decode call (split kernel + logsumexp combine) with every
+input resident in HBM. The prefill half of the metric is measured on the mixed
+step's prefill rows (4 chunks of 2048 queries, priors ~ U{0..6144}, global and
+local families) and reported alongside.
+
+Prints one JSON line (rank 0). value = decode KV GB/s over the timed steps:
+KV bytes = sum over rows and KV heads of visible keys * head_dim * 2 B * 2 (K, V).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% bf16 MFMA peak)"
+DECODE_KERNEL = "decode_split_kernel<512, false>"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-flushed", action="store_true",
+                   help="skip the MALL-flushed re-measurement (profiling runs: keeps every decode launch "
+                        "in the kernel trace identical to the timed ones)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run only a 1 GiB device copy (counter calibration for FETCH_SIZE / WRITE_SIZE)")
+    return p.parse_args()
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h", "combine.hip"):
+        with open(os.path.join(ROOT, "global_paged_gqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest):
+    """HBM bytes per decode-kernel launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_global_b32_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calib_copy():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "launches": 5}))
+
+
+def cpu_baseline(batch, kv_bytes):
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attend_batch(batch)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or reps >= 50:
+            break
+    return {"value": round(kv_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"the full 32-row global decode batch, {reps} pass(es) in {el:.1f} s "
+                      f"(fp64 two-pass softmax over contiguous K/V, OpenMP over (query, head))"}
+
+
+def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
+    out = {}
+    for fam in ("global", "local"):
+        pre, _ = workloads.cfg4_mixed(fam)
+        d = devio.DeviceBatch(pre)
+        d.prefill()
+        torch.cuda.synchronize()
+        s = pre.spec
+        flops = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens, pre.q_lens)
+        ts = []
+        for _ in range(iters):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            d.prefill()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        ts.sort()
+        t = ts[len(ts) // 2]
+        tf = flops / t / 1e12
+        out[fam] = {"tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "ms": round(t * 1e3, 4), "flops": flops,
+                    "workload": f"{fam}: 4 chunks x 2048 queries, priors {pre.ctx_lens.tolist()}"}
+        del d
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+              "path: rows shard across GPUs with no attention-side communication.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import workloads
+    from global_paged_gqa_amd import devio, traffic
+
+    batch = workloads.cfg2_global_decode()
+    s = batch.spec
+    split = 512
+    kv_bytes = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared,
+                                       batch.ctx_lens)
+    d = devio.DeviceBatch(batch)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        d.decode(split)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` back-to-back steps, per-step events on the library's stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        d.decode(split)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+    ms_per_step = wall / args.steps * 1e3
+    value = kv_bytes * args.steps / wall / 1e9
+
+    # the combine alone on the same partials, to separate the split kernel's own duration
+    nat = devio.nat
+    ns = nat.gattn_decode_workspace_bytes(d.layer, batch.B, int(batch.ctx_lens.max()), split) // (4 * (s.head_dim + 1) * batch.B * s.num_q_heads)
+    o_part = d.workspace[: batch.B * s.num_q_heads * ns * s.head_dim]
+    lse_part = d.workspace[batch.B * s.num_q_heads * ns * s.head_dim:]
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for e0, e1 in cevs:
+        e0.record(stream)
+        nat.gattn_combine(batch.B, s.num_q_heads, s.head_dim, ns, o_part, lse_part, d.out, d.lse, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    combine_s = sum(e0.elapsed_time(e1) for e0, e1 in cevs) * 1e-3 / len(cevs)
+    split_kernel_s = sum(step_s) / len(step_s) - combine_s
+    achieved = kv_bytes / split_kernel_s / 1e9
+
+    # the same step with the 256 MB MALL flushed before each launch (outside the events)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flushed = None
+    if not args.no_flushed:
+        fl = []
+        for _ in range(20):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            d.decode(split)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            fl.append(e0.elapsed_time(e1) * 1e-3)
+        fl.sort()
+        fgbs = kv_bytes / fl[len(fl) // 2] / 1e9
+        flushed = {"decode_gbs": round(fgbs, 1), "frac": round(fgbs / HBM_PEAK_GBS, 4)}
+
+    digest = kernel_source_digest()
+    traffic_bytes = measured_traffic(digest)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "global-family split-KV decode: batch 32, 32 q heads, 4 KV heads, head_dim 512, "
+                               "contexts ~U{1..8192}, page 16, shuffled pages, split 512",
+                   "batch": batch.B, "head_dim": s.head_dim, "num_q_heads": s.num_q_heads,
+                   "num_kv_heads": s.num_kv_heads, "split_tokens": split,
+                   "kv_bytes_per_step": kv_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_bytes, "kernel_us": round(split_kernel_s * 1e6, 2),
+                     "combine_us": round(combine_s * 1e6, 2), "kernel_source_digest": digest},
+        "mall_flushed": flushed,
+    }
+    if not args.no_prefill:
+        try:
+            result["prefill"] = prefill_measure(torch, devio, workloads, traffic, flush)
+        except Exception as e:  # report, never hide
+            result["prefill"] = {"error": str(e)[:200]}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(batch, kv_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
