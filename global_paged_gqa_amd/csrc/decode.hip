@@ -9,19 +9,23 @@
 // tile pruning that page 5's "Three load-bearing facts" #1 credits with a 3-4x
 // gain).
 //
-// Inside the workgroup four waves take the split's pages round-robin. Each wave
-// keeps its own online-softmax state for the g query heads that share this KV
-// head and merges with the other three at the end through LDS, in a fixed order
-// (deterministic, so results are bitwise independent of the batch).
+// Work split inside the workgroup (four waves): a wave owns 256 head dims of
+// the pages of its page group. With head_dim 256 there are four page groups of
+// one wave each; with head_dim 512 there are two groups of two waves, the pair
+// splitting the head dims and adding their partial scores through LDS (one
+// barrier per page). Each group keeps its own online-softmax state for the g
+// query heads sharing this KV head; the groups merge at the end through LDS in
+// a fixed order, so results are bitwise independent of the batch.
 //
-// Per page (16 tokens) a wave does, entirely in registers:
-//   S^T[16 tok][16 heads] = K[16 tok][hd] . Q^T[hd][16 heads]   (MFMA 16x16x32, bf16)
-//   online softmax on S^T columns                                 (VALU + lane swaps)
+// Per page (16 tokens) a wave does, in registers:
+//   S^T[16 tok][16 heads] = K[16 tok][dims] . Q^T[dims][16 heads]   (MFMA 16x16x32, bf16)
+//   online softmax on S^T columns                                     (VALU + lane shuffles)
 //   V^T tile = MFMA(V, identity)  -- an exact register transpose of V
-//   O^T[hd][16 heads] += V^T[hd][16 tok] . P^T[16 tok][16 heads]  (MFMA 16x16x16, bf16)
-// The K/V loads are 16 B per lane straight from the page into the MFMA operand
-// layout (each instruction reads 64 contiguous bytes of 16 token rows), with the
-// next page's loads in flight while the current page is computed.
+//   O^T[dims][16 heads] += V^T[dims][16 tok] . P^T[16 tok][16 heads]  (MFMA 16x16x16, bf16)
+// K/V are read 16 B per lane straight from the page into the MFMA operand layout
+// (each instruction reads 64 contiguous bytes of 16 token rows), one page ahead
+// of the math, through buffer loads whose resource has zero size past the end of
+// the wave's page list (no traffic, no fault, no conditional load).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,27 +35,33 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kDimsPerWave = 256;
 constexpr int kMergeBytes = 32 * 1024;
+constexpr int kOcc = 2;  // workgroups per CU the register budget is sized for
 
-template <int HD>
 struct PageRegs {
-    u32x4 r[HD / 32];
+    u32x4 r[kDimsPerWave / 32];
 };
 
-template <int HD, bool SHARED>
-__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
-    constexpr int NS = HD / 32;  // K-steps of 32 dims for QK
-    constexpr int NT = HD / 16;  // 16-dim tiles of the output
+template <int HD, bool SHARED, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(DecodeArgs a) {
+    constexpr int DS = HD / kDimsPerWave;      // waves sharing one page (1 or 2)
+    constexpr int NGRP = kWaves / DS;          // page groups
+    constexpr int NS = kDimsPerWave / 32;      // K-steps of 32 dims for QK, per wave
+    constexpr int NT = kDimsPerWave / 16;      // 16-dim output tiles, per wave
+    constexpr int kQStride = HD + 8;           // padded LDS row (bf16 elements) of one head's query
+    constexpr int kChunk = kMergeBytes / 4 / (NGRP * HD);  // heads merged per round
 
-    constexpr int kQStride = HD + 8;  // padded LDS row (bf16 elements) of one head's query
     __shared__ float sm_o[kMergeBytes / 4];
     __shared__ __attribute__((aligned(16))) uint16_t sm_q[16 * kQStride];
-    __shared__ float sm_m[kWaves][16];
-    __shared__ float sm_l[kWaves][16];
+    __shared__ f32x4 sm_s[DS > 1 ? 2 : 1][DS > 1 ? kWaves * 64 : 1];  // partial scores, double-buffered
+    __shared__ float sm_m[NGRP][16];
+    __shared__ float sm_l[NGRP][16];
     __shared__ int sm_bad[kWaves];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / DS, dpart = wave % DS;
     const int c16 = lane & 15;  // MFMA row/column index of this lane
     const int r4 = lane >> 4;   // 16-lane row of this lane
     const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -79,19 +89,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 
     const int pg0 = tb / kPage, pg1 = (te - 1) / kPage;
     const int npg = bad_len ? 0 : pg1 - pg0 + 1;
-    const int cnt = npg > wave ? (npg - wave + kWaves - 1) / kWaves : 0;
+    const int cnt = npg > grp ? (npg - grp + NGRP - 1) / NGRP : 0;  // pages of this group
+    const int cnt_max = (npg + NGRP - 1) / NGRP;                       // of the largest group
+    // Paired waves meet at a barrier every page, so every wave runs the same trip count.
+    const int trips = DS > 1 ? cnt_max : cnt;
+
+    const int64_t blk = (int64_t)kPage * HD;  // elements of one (page, KV head) block
+    const uint32_t lane_off = (uint32_t)(c16 * HD + dpart * kDimsPerWave + r4 * 8) * 2u;  // bytes
+    const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
+    const int pg_hi = npg > 0 ? pg1 : 0;  // last page-table entry this workgroup may read
+    auto page_of = [&](int i) { return pg0 + grp + NGRP * i; };
+
+    // ---- page ids, 64 at a time in one vector register: lane j holds the id of the group's
+    // page 64*k + j. Pages read their id back with readlane, so no page waits on a scalar
+    // load; the next 64 ids are fetched one block ahead. Out-of-range indices are clamped to
+    // an entry the workgroup owns (their ids are never used).
+    auto load_ids = [&](int first) { return pt[min(page_of(first + lane), pg_hi)]; };
+    int ids = load_ids(0);
+    int ids_next = load_ids(64);
 
     // ---- Q^T as the B operand, staged once in LDS for the 16 MFMA columns (the g real
     // heads, zeros for the rest); each page reads lane's head c16, 8 dims per K-step.
-    for (int e = threadIdx.x; e < 16 * (HD / 8); e += kThreads) {
+    constexpr int kQItems = 16 * (HD / 8) / kThreads;
+    u32x4 qv[kQItems];
+#pragma unroll
+    for (int k = 0; k < kQItems; ++k) {
+        const int e = threadIdx.x + k * kThreads;
         const int hn = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (hn < g)
-            v = *(const u32x4 *)(a.q + ((int64_t)b * Hq + kvh * g + hn) * HD + d8);
-        *(u32x4 *)(sm_q + hn * kQStride + d8) = v;
+        // unconditional load of a valid head, zeroed afterwards for the padding columns
+        const u32x4 v = *(const u32x4 *)(a.q + ((int64_t)b * Hq + kvh * g + min(hn, g - 1)) * HD + d8);
+        qv[k] = hn < g ? v : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();
-    const uint16_t *q_lane = sm_q + c16 * kQStride + r4 * 8;
+    const uint16_t *q_lane = sm_q + c16 * kQStride + dpart * kDimsPerWave + r4 * 8;
     // Identity blocks for the register transpose: B[(r4, e)][c16] = 1 iff 8*r4 + e == 16*h + c16.
     u32x4 ident[2];
 #pragma unroll
@@ -114,39 +143,45 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     float m_run = -INFINITY, l_run = 0.f;
     int bad_page = 0;
 
-    const int64_t blk = (int64_t)kPage * HD;  // elements of one (page, KV head) block
-    const int lane_off = c16 * HD + r4 * 8;
-    const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
-
-    auto page_of = [&](int i) { return pg0 + wave + kWaves * i; };
-    auto page_id = [&](int i) {  // scalar load of a page id (wave-uniform), checked
-        int pid = i < cnt ? pt[page_of(i)] : 0;
-        if (pid < 0 || pid >= a.num_pages) {
+    // Buffer resource of this KV head's block in page i of the group's list. Past the end of
+    // the list, or for a page id outside the pool, the resource has zero size: its loads
+    // return zeros without touching memory, so every load can be issued unconditionally
+    // (which keeps the compiler's wait counts exact across the software pipeline).
+    auto page_rsrc = [&](const uint16_t *pool, int i, int ib) {
+        const int rel = i - ib;  // 0..65: position in ids (or, past 63, in ids_next)
+        int pid = __builtin_amdgcn_readlane(rel >= 64 ? ids_next : ids, rel & 63);
+        bool live = i < cnt;
+        if (live && (pid < 0 || pid >= a.num_pages)) {
             bad_page = 1;
-            pid = 0;
+            live = false;
         }
-        return pid;
+        if (!live)
+            pid = 0;
+        const uint16_t *base = pool + ((int64_t)pid * a.num_kv_heads + kvh) * blk;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, live ? (int)(blk * 2) : 0, 0x00020000);
     };
-    auto load_k = [&](PageRegs<HD> &K, int pid) {
-        const uint16_t *kp = a.k_pool + ((int64_t)pid * a.num_kv_heads + kvh) * blk + lane_off;
+    auto load_regs = [&](PageRegs &R, __amdgpu_buffer_rsrc_t rsrc) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            K.r[s] = *(const u32x4 *)(kp + s * 32);
+            R.r[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, s * 64, 0));
+        __builtin_amdgcn_sched_barrier(0);  // keep the whole page's loads ahead of the math
     };
-    auto load_v = [&](PageRegs<HD> &V, int pid) {
-        const uint16_t *vp = a.v_pool + ((int64_t)pid * a.num_kv_heads + kvh) * blk + lane_off;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            V.r[s] = *(const u32x4 *)(vp + s * 32);
-    };
-    // Scores of page i, online-softmax update, rescale of the accumulator; returns P^T
-    // (bf16, as the B operand of the PV product) and which of the lane's tokens are valid.
-    auto qk_softmax = [&](PageRegs<HD> &K, int i, bool (&valid)[4]) {
+    // Scores of page i (this wave's dims; with paired waves the two halves are added in a
+    // fixed order, low dims first), online-softmax update and rescale of the accumulator.
+    // Returns P^T (bf16, the B operand of the PV product) and the lane's valid tokens.
+    auto qk_softmax = [&](PageRegs &K, int i, bool (&valid)[4]) {
         const int t0 = page_of(i) * kPage;
         f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
             st = mfma_k32(K.r[s], *(const u32x4 *)(q_lane + s * 32), st);
+        if (DS > 1) {
+            f32x4 *buf = sm_s[i & 1];
+            buf[wave * 64 + lane] = st;
+            __syncthreads();
+            const f32x4 other = buf[(wave ^ 1) * 64 + lane];
+            st = dpart == 0 ? st + other : other + st;
+        }
         // lane holds S^T[token t0 + 4*r4 + e][head c16]; out-of-range tokens are selected
         // out (a NaN in an unused slot never reaches the sums)
         float mx = -INFINITY;
@@ -178,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
         return u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
     };
     // O^T += V^T P^T for page i; V^T comes from an exact MFMA transpose of the V registers.
-    auto pv = [&](PageRegs<HD> &V, int i, u32x2 pb, const bool (&valid)[4]) {
+    auto pv = [&](PageRegs &V, int i, u32x2 pb, const bool (&valid)[4]) {
         const int t0 = page_of(i) * kPage;
         const bool edge = t0 < tb || t0 + kPage > te;  // page holds tokens outside [tb, te)
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -203,78 +238,89 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    // One page of the group: its scores (always, so paired waves meet at their barrier),
+    // then the softmax update and PV product if the page exists for this group.
+    auto page_step = [&](PageRegs &K, PageRegs &V, int i) {
+        bool valid[4];
+        if (DS > 1 && i >= cnt) {  // dummy trip: only the partial-score exchange
+            f32x4 *buf = sm_s[i & 1];
+            buf[wave * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+            __syncthreads();
+            return;
+        }
+        const u32x2 pb = qk_softmax(K, i, valid);
+        pv(V, i, pb, valid);
+    };
 
-    // Pipeline: page ids two pages ahead, K one page ahead of the math. V is either
-    // double-buffered like K (VBUF = 2) or loaded into its single buffer right after the
-    // previous page's PV product (VBUF = 1, for the largest register footprint).
-    constexpr int VBUF = (SHARED || HD <= 256) ? 2 : 1;
-    if (cnt > 0) {
-        PageRegs<HD> KA, KB, VA, VB;
-        int pid_b = page_id(1);
-        {
-            const int pid_a = page_id(0);
-            load_k(KA, pid_a);
-            if (!SHARED)
-                load_v(VA, pid_a);
+    // ---- pipeline: K one page ahead of the math; V too when there is room (VBUF = 2),
+    // otherwise V's single buffer is refilled right after each PV product (VBUF = 1)
+    constexpr int VBUF = (SHARED || OCC == 1) ? 2 : 1;
+    PageRegs KA, KB, VA, VB;
+    load_regs(KA, page_rsrc(a.k_pool, 0, 0));  // unconditional: empty resource when cnt == 0
+    if (!SHARED)
+        load_regs(VA, page_rsrc(a.v_pool, 0, 0));
+#pragma unroll
+    for (int k = 0; k < kQItems; ++k) {
+        const int e = threadIdx.x + k * kThreads;
+        *(u32x4 *)(sm_q + (e / (HD / 8)) * kQStride + (e % (HD / 8)) * 8) = qv[k];
+    }
+    __syncthreads();
+
+    for (int i = 0; i < trips; i += 2) {
+        // page ids: the block of 64 holding page i is `ids`, the following block `ids_next`
+        if ((i & 63) == 0 && i > 0) {
+            ids = ids_next;
+            ids_next = load_ids(i + 64);
         }
-        for (int i = 0; i < cnt; i += 2) {
-            const int pid_c = page_id(i + 2);
-            bool valid[4];
-            // page i in KA/VA; page i+1 goes to KB (and VB, or VA after the PV product)
-            if (i + 1 < cnt) {
-                load_k(KB, pid_b);
-                if (!SHARED && VBUF == 2)
-                    load_v(VB, pid_b);
-            }
-            u32x2 pb = qk_softmax(KA, i, valid);
-            pv(SHARED ? KA : VA, i, pb, valid);
-            if (i + 1 >= cnt)
-                break;
-            if (!SHARED && VBUF == 1)
-                load_v(VA, pid_b);
-            // page i+1 in KB/(VB or VA); page i+2 goes to KA (and VA)
-            if (i + 2 < cnt) {
-                load_k(KA, pid_c);
-                if (!SHARED && VBUF == 2)
-                    load_v(VA, pid_c);
-            }
-            pb = qk_softmax(KB, i + 1, valid);
-            pv(SHARED ? KB : (VBUF == 2 ? VB : VA), i + 1, pb, valid);
-            if (!SHARED && VBUF == 1 && i + 2 < cnt)
-                load_v(VA, pid_c);
-            pid_b = page_id(i + 3);
-        }
+        const int ib = i & ~63;  // page index of ids' lane 0
+        // page i in KA/VA; page i+1 goes to KB (and VB, or VA after the PV product)
+        load_regs(KB, page_rsrc(a.k_pool, i + 1, ib));
+        if (!SHARED && VBUF == 2)
+            load_regs(VB, page_rsrc(a.v_pool, i + 1, ib));
+        page_step(KA, SHARED ? KA : VA, i);
+        if (!SHARED && VBUF == 1)
+            load_regs(VA, page_rsrc(a.v_pool, i + 1, ib));
+        if (i + 1 >= trips)
+            break;
+        // page i+1 in KB/(VB or VA); page i+2 goes to KA (and VA)
+        load_regs(KA, page_rsrc(a.k_pool, i + 2, ib));
+        if (!SHARED && VBUF == 2)
+            load_regs(VA, page_rsrc(a.v_pool, i + 2, ib));
+        page_step(KB, SHARED ? KB : (VBUF == 2 ? VB : VA), i + 1);
+        if (!SHARED && VBUF == 1)
+            load_regs(VA, page_rsrc(a.v_pool, i + 2, ib));
     }
 
-    // ---- merge the four waves (fixed order) and write this split's result
-    if (r4 == 0) {
-        sm_m[wave][c16] = m_run;
-        sm_l[wave][c16] = l_run;
+    // ---- merge the page groups (fixed order) and write this split's result
+    if (dpart == 0 && r4 == 0) {
+        sm_m[grp][c16] = m_run;
+        sm_l[grp][c16] = l_run;
     }
     if (lane == 0)
         sm_bad[wave] = bad_page;
-    const bool any_bad = bad_len;
-    constexpr int kChunk = kMergeBytes / 4 / (kWaves * HD);  // heads merged per round
     for (int h0 = 0; h0 < g; h0 += kChunk) {
         __syncthreads();
         if (c16 >= h0 && c16 < min(g, h0 + kChunk)) {
-            float *dst = sm_o + ((wave * kChunk) + (c16 - h0)) * HD + 4 * r4;
+            float *dst = sm_o + (grp * kChunk + (c16 - h0)) * HD + dpart * kDimsPerWave + 4 * r4;
 #pragma unroll
             for (int j = 0; j < NT; ++j)
                 *(f32x4 *)(dst + 16 * j) = acc[j];
         }
         __syncthreads();
-        const bool bad = any_bad || sm_bad[0] || sm_bad[1] || sm_bad[2] || sm_bad[3];
+        bool bad = bad_len;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            bad = bad || sm_bad[w];
         const int nh = min(g, h0 + kChunk) - h0;
         for (int e = threadIdx.x; e < nh * HD; e += kThreads) {
             const int hn = h0 + e / HD, d = e % HD;
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w)
+            for (int w = 0; w < NGRP; ++w)
                 M = fmaxf(M, sm_m[w][hn]);
             float lsum = 0.f, o = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < NGRP; ++w) {
                 const float mw = sm_m[w][hn];
                 if (mw == -INFINITY)
                     continue;
@@ -305,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 template <int HD, bool SHARED>
 hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0,
+    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, kOcc>, grid, dim3(kThreads), args, 0,
                            stream);
 }
 
