@@ -14,8 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
 SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip"]
 # MFMA results and accumulators in VGPRs (AGPRs then serve as spill space): the
-# decode kernels otherwise keep copies of the accumulator in both register files.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# attention kernels otherwise keep copies of the accumulator in both register files.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
