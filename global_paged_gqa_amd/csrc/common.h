@@ -62,6 +62,16 @@ __device__ __forceinline__ float rows_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at lds + 16 * l
+// (lds must be wave-uniform). The host compilation pass never sees the builtin, whose
+// LDS pointer type has no host meaning.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0,
+                                             0, 0);
+#endif
+}
+
 // NaN-propagating max (fmaxf would drop a NaN operand).
 __device__ __forceinline__ float nan_max(float a, float b) { return (a > b || a != a) ? a : b; }
 
