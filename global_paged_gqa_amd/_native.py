@@ -14,6 +14,12 @@ LIB_PATH = os.path.join(_HERE, "libgattn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the gfx950 library first "
                       "(python -c 'import __graft_entry__ as g; g.build()')")
+# torch ships its own HIP runtime (soname libamdhip64.so.7). Loading torch first makes the
+# library's libamdhip64.so.7 dependency resolve to that same runtime; loaded the other way
+# round, the process holds two runtimes and torch's streams are not valid handles in the one
+# the library launches on (every launch then fails).
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 LOCAL, GLOBAL = 0, 1

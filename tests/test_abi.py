@@ -162,3 +162,13 @@ def test_prefill_and_combine_reject_bad_arguments():
     assert st(g.gattn_combine, 4, 32, 510, 3, 1, 2, 3, 4) == nat.ERR_UNSUPPORTED
     assert st(g.gattn_combine, 4, 32, 512, 3, None, 2, 3, 4) == nat.ERR_NULL_PTR
     assert st(g.gattn_combine, 0, 32, 512, 3, 1, 2, 3, 4) == 0
+
+
+def test_one_hip_runtime_in_process():
+    """The library must bind the HIP runtime torch uses: two runtimes in one process make
+    torch's stream handles invalid for the library's launches."""
+    import re
+    maps = open("/proc/self/maps").read()
+    libs = {os.path.basename(p).split(".so")[0] + "|" + os.path.dirname(p)
+            for p in re.findall(r"\S*libamdhip64\.so\S*", maps)}
+    assert len(libs) <= 1, libs
