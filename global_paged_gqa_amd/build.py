@@ -13,10 +13,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
 SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip"]
-# MFMA results and accumulators in VGPRs (AGPRs then serve as spill space): the
-# attention kernels otherwise keep copies of the accumulator in both register files.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# MFMA results and accumulators in VGPRs (AGPRs then serve as spill space): the decode
+# kernels otherwise keep copies of the accumulator in both register files. (The prefill
+# kernel keeps its output accumulators in AGPRs.)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 

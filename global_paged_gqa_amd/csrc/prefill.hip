@@ -2,29 +2,35 @@
 //
 // A chunk's queries attend the cache with the causal mask inside the chunk and the
 // sliding window for the local family (Core AI card, "Contents": a flash-prefill
-// with a query axis and an intra-chunk causal mask). One workgroup = one (row,
-// KV head, query tile) of 64 or 128 MFMA rows; the g query heads that share the KV head
-// are packed into the rows (row m = position m / g, head m % g), so every K/V byte
+// with a query axis and an intra-chunk causal mask). One workgroup = one (row, KV
+// head, query tile) of 128 MFMA rows; the g query heads that share the KV head are
+// packed into the rows (row m = query position m / g, head m % g), so every K/V byte
 // staged in LDS serves all g heads.
 //
-// Each wave owns 16 or 32 rows (one or two 16-row MFMA tiles) and the full head_dim;
-// with two tiles every K/V operand read from LDS feeds two MFMAs. K/V pages stream
-// through a ring of LDS stages filled by direct global->LDS buffer loads (no
-// registers in flight), several pages ahead of the math; one barrier per page.
-// The key range of a tile is pruned to [first visible key of its first query, its
-// last query]: pages outside the window are never read (page 5's "Three
-// load-bearing facts" #1: sliding-window tile pruning).
+// Keys are processed in blocks of 32 tokens (two pages). Both products use the
+// 32x32x16 bf16 MFMA, which runs at the full matrix rate on gfx950 (the 16x16x16 form
+// runs at half rate):
+//   QK: wave w computes S^T[32 tok][32 rows] = K . Q^T for its own 32 rows over the whole
+//       head_dim (A = K from LDS, B = Q^T kept in registers), then the masked online
+//       softmax of those rows.
+//   P exchange: each wave stores its P^T as bf16 in LDS, already in the lane order of the
+//       PV product's B operand, plus the rows' rescale factors.
+//   PV: wave w owns head_dim/4 output dims for all 128 rows: O^T[dims][rows] += V^T . P^T,
+//       with V^T read from the row-major page by the gfx950 transpose read
+//       (ds_read_b64_tr_b16). Every V^T fragment feeds four MFMAs (the four row tiles).
+// K and V blocks stream through a 128 KB LDS ring filled by direct global->LDS buffer
+// loads several blocks ahead; two barriers per block (one also publishes P).
 //
-// Per KV page (16 tokens), per wave and 16-row tile:
-//   S^T[16 tok][16 rows] = K . Q^T     MFMA 16x16x32; K from LDS (XOR-swizzled rows),
-//                                      Q^T in registers
-//   causal / window mask, online softmax per row (columns of S^T)
-//   O^T[hd][16 rows] += V^T . P^T      MFMA 16x16x16; V^T read from the row-major LDS
-//                                      page with the gfx950 transpose read
-//                                      (ds_read_b64_tr_b16), P^T straight from S^T's
-//                                      accumulator layout
-// Workgroups are mapped so that each XCD works through contiguous query tiles of
-// the same (row, KV head), which then share that XCD's L2.
+// The online softmax rescales lazily: a row keeps its running maximum until a new score
+// exceeds it by more than 2^8, so P stays below 256 and the accumulators are rescaled only
+// on those (rare) blocks. The final O = acc / l and LSE = m + log2 l use the same maximum,
+// so the result is the exact softmax up to rounding.
+//
+// The key range of a tile is pruned to [first visible key of its first query, its last
+// query] (page 5's "Three load-bearing facts" #1: sliding-window tile pruning); pages in a
+// block that lie outside it are never read (zero-size buffer resource: zeros, no traffic).
+// Workgroups are mapped so that each XCD works through the query tiles of the same (row,
+// KV head), heaviest first, sharing that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,34 +39,33 @@ namespace gattn {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 128;          // MFMA rows per workgroup (4 tiles of 32)
+constexpr int kTok = 32;            // keys per block (two pages)
+constexpr int kRingBytes = 128 * 1024;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// Work split per head dim. head_dim 256: four waves of two 16-row tiles (every K/V operand
-// read from LDS feeds two MFMAs), 128 rows per workgroup. head_dim 512: four waves of one
-// tile, 64 rows per workgroup, which keeps the 512-dim accumulator and Q^T of a wave in its
-// registers with no spill. One wave per SIMD in both.
-template <int HD>
-struct Shape {
-    static constexpr int RT = HD == 256 ? 2 : 1;  // 16-row MFMA tiles per wave
-    static constexpr int WAVES = 4;
-    static constexpr int THREADS = WAVES * 64;
-    static constexpr int ROWS = WAVES * RT * 16;   // MFMA rows per workgroup
-};
-
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-// Byte offset of 16-byte chunk `c` of token row `t` inside one staged (page, KV head)
-// block: rows of HD*2 bytes, chunks XOR-swizzled by the token so 16 rows read at the
-// same logical chunk land in 16 different bank groups.
-template <int HD>
-__device__ __forceinline__ uint32_t chunk_off(int t, int c) {
-    return (uint32_t)(t * HD * 2 + ((c ^ (t & 15)) << 4));
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
 }
 
-// The ring's direct buffer->LDS loads and the waits on them are written as inline assembly,
-// so that the compiler neither orders its own LDS reads behind every in-flight ring load nor
-// merges the ring's wait with its own counters: the ring is synchronised by exactly one
-// "at most N loads outstanding" wait plus a barrier per page.
+// LDS layout of one unit (the K or the V of one 32-token block): token row t at t * HD * 2
+// bytes, its 16-byte chunk c at slot c ^ swz(t & 15). swz is a bit permutation of the low
+// four token bits chosen so that (i) the 16 tokens read at one chunk by a K operand load
+// hit 16 different 16-byte bank groups and (ii) the four tokens x two chunks of one
+// transpose-read lane group hit 8 different ones.
+__device__ __forceinline__ int swz(int x) { return ((x & 3) << 1) | ((x >> 2) & 1) | (x & 8); }
+
+// The ring's direct buffer->LDS loads and the waits on them are inline assembly: the
+// compiler sees neither, so it never orders its own LDS reads behind in-flight ring loads;
+// the ring is synchronised by exactly one "at most N loads outstanding" wait plus a barrier
+// per unit.
 //
 // 16 bytes per lane from the buffer `rsrc` at byte offset voffset into LDS at lds + 16 * lane
 // (M0 holds the LDS base; it is saved and restored around the load).
@@ -89,54 +94,91 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes) {
     return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, bytes, 0x00020000u};
 }
 
-// ds_read_b64_tr_b16 of four V^T tiles, then one wait for all of them. The ring's LDS reads
-// are inline assembly as well (their ordering after the page they read is the ring wait plus
-// barrier); the "+v" operands of the wait keep every use of a result after it.
-__device__ __forceinline__ void tr_read4(u32x2 (&v)[4], const uint8_t *base, uint32_t off0, uint32_t step) {
-    const uint32_t a0 = (uint32_t)(uintptr_t)base;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v[k]) : "v"(a0 + (off0 ^ (step * k))));
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+// Four K-steps of the score product S^T += K . Q^T in VGPRs. The PV accumulators fill the
+// AGPR file, so the score tile must live in VGPRs; the compiler would place any MFMA result
+// in AGPRs here, hence assembly. Back-to-back MFMAs accumulating into exactly the same
+// registers need no wait states; `first` starts from zero instead of reading S^T.
+template <bool first>
+__device__ __forceinline__ void qk4(f32x16 &st, u32x4 k0, u32x4 k1, u32x4 k2, u32x4 k3, u32x4 q0, u32x4 q1,
+                                    u32x4 q2, u32x4 q3) {
+    if (first)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %5, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0"
+            : "=&v"(st)
+            : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(q0), "v"(q1), "v"(q2), "v"(q3));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %5, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0"
+            : "+v"(st)
+            : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(q0), "v"(q1), "v"(q2), "v"(q3));
 }
 
-// Two ds_read_b128 (K operands, `step` apart under the XOR swizzle), then one wait.
-__device__ __forceinline__ void k_read2(u32x4 (&v)[2], const uint8_t *base, uint32_t off0, uint32_t step) {
-    const uint32_t a0 = (uint32_t)(uintptr_t)base;
+// The wait states an MFMA result needs before a vector instruction may read it (the
+// compiler cannot see that qk4 is an MFMA), with margin.
+__device__ __forceinline__ void qk_settle(f32x16 &st) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(st));
+}
+
+// acc *= al for an accumulator tile held in AGPRs, one register at a time through a single
+// VGPR (written in C++ the multiply makes the compiler stage whole tiles in VGPRs). The
+// trailing wait states separate the AGPR writes from the next MFMA reading them.
+__device__ __forceinline__ void scale_acc(f32x16 &c, float al) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-        asm volatile("ds_read_b128 %0, %1" : "=v"(v[k]) : "v"(a0 + (off0 ^ (step * k))));
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]));
+    for (int v = 0; v < 16; v += 4) {
+        float x0 = c[v], x1 = c[v + 1], x2 = c[v + 2], x3 = c[v + 3], t;
+        asm volatile(
+            "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
+            "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
+            "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
+            "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4\n\t"
+            "s_nop 4"
+            : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t)
+            : "v"(al));
+        c[v] = x0;
+        c[v + 1] = x1;
+        c[v + 2] = x2;
+        c[v + 3] = x3;
+    }
+}
+
+__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
 }
 
 template <int HD, bool SHARED>
-__global__ __launch_bounds__(Shape<HD>::THREADS, 1) void prefill_kernel(PrefillArgs a) {
-    constexpr int kRT = Shape<HD>::RT;
-    constexpr int kThreads = Shape<HD>::THREADS;
-    constexpr int kRows = Shape<HD>::ROWS;
-    constexpr int NS = HD / 32;                       // K-steps of the score product
-    constexpr int NT = HD / 16;                       // 16-dim output tiles
-    constexpr int BLOCK = kPage * HD * 2;             // bytes of one (page, KV head) block
-    constexpr int STAGE = SHARED ? BLOCK : 2 * BLOCK; // K (and V) of one page
-    constexpr int NSTAGE = 128 * 1024 / STAGE;          // ring depth (pages)
-    constexpr int LPB = BLOCK / 16 / kThreads;        // 16-byte loads per lane per block
-    constexpr int LPP = SHARED ? LPB : 2 * LPB;       // ... per page
-    static_assert(NSTAGE >= 3, "ring too shallow");
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+    constexpr int NKS = HD / 16;                     // K-steps of the score product
+    constexpr int DW = HD / kWaves;                  // output dims per wave in PV
+    constexpr int ND = DW / 32;                      // 32-dim output tiles per wave
+    constexpr int UNIT = kTok * HD * 2;              // bytes of the K (or V) of one block
+    constexpr int NU = kRingBytes / UNIT;            // ring depth in units
+    constexpr int LPU = UNIT / 16 / kThreads;        // 16-byte loads per lane per unit
+    constexpr int PAGE_BYTES = kPage * HD * 2;       // one (page, KV head) block
+    static_assert(NU >= 3 && LPU % 2 == 0, "ring shape");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE][STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t p_lds[kWaves * 2 * 64 * 16];  // P^T fragments
+    __shared__ float alpha_lds[kRows];
+    __shared__ float l_lds[kRows];
+    __shared__ int flag_lds[kWaves];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c16 = lane & 15, r4 = lane >> 4;
+    const int n32 = lane & 31, h = lane >> 5;
     const int g = a.group, Hq = a.num_q_heads;
 
     // ---- XCD-aware work mapping: the dispatcher deals workgroups round-robin over the
-    // XCDs, so give XCD x a contiguous run of work items (query tile fastest).
+    // XCDs, so give XCD x a contiguous run of work items; within a (row, KV head) the query
+    // tiles run from the last (most keys) to the first.
     const int nwg = gridDim.x * gridDim.y * gridDim.z;
     const int wid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int xcd = wid % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
     const int item = xcd * per + min(xcd, extra) + wid / kXcds;
-    const int qt = item % gridDim.x;
+    const int qt = gridDim.x - 1 - item % gridDim.x;
     const int kvh = (item / gridDim.x) % gridDim.y;
     const int b = item / (gridDim.x * gridDim.y);
 
@@ -152,242 +194,319 @@ __global__ __launch_bounds__(Shape<HD>::THREADS, 1) void prefill_kernel(PrefillA
     // Malformed rows (more queries than cached tokens, or a cache beyond the table)
     // produce NaN outputs instead of reading outside the table.
     const bool bad_row = q_len > L || (L - 1) / kPage >= a.pt_stride;
-    const int lo = a.is_global ? 0 : max(0, p_first - a.window + 1);
-    const int pg0 = lo / kPage, pg1 = p_last / kPage;
-    const int npg = bad_row ? 0 : pg1 - pg0 + 1;
+    const int lo = a.is_global ? 0 : max(0, p_first - a.window + 1);  // first key any row sees
+    const int kb0 = lo & ~(kTok - 1);                                    // first block's first key
+    const int nblk = bad_row ? 0 : (p_last - kb0) / kTok + 1;
+    const int pgA = kb0 / kPage;                                         // first page of block 0
+    const int npg = bad_row ? 0 : p_last / kPage - pgA + 1;
     const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
 
-    // ---- this wave's rows: tile rt, lane c16 -> row m -> (query tile_q + m / g, head m % g)
-    int row_pos[kRT], row_head[kRT], p_row[kRT], lo_row[kRT];
-    bool row_ok[kRT];
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-        const int m = (wave * kRT + rt) * 16 + c16;
-        row_pos[rt] = m / g;
-        row_head[rt] = m % g;
-        row_ok[rt] = row_pos[rt] < nq;
-        p_row[rt] = p_first + row_pos[rt];
-        lo_row[rt] = a.is_global ? 0 : p_row[rt] - a.window + 1;
-    }
+    // ---- this wave's score rows (QK / softmax): row m = 32 * wave + n32
+    const int m_own = 32 * wave + n32;
+    const int pos_own = m_own / g;
+    const bool ok_own = pos_own < nq;
+    const int p_own = p_first + pos_own;
 
-    // ---- Q^T as the B operand: lane holds row c16, 8 dims per K-step (zeros for padding rows)
-    u32x4 qb[kRT][NS];
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
+    // ---- Q^T as the B operand: lane holds row n32, dims 16 s + 8 h .. +7 (zeros for padding rows)
+    u32x4 qb[NKS];
+    {
         const uint16_t *qp =
-            a.q + ((int64_t)(q0 + tile_q + (row_ok[rt] ? row_pos[rt] : 0)) * Hq + kvh * g + row_head[rt]) * HD + r4 * 8;
+            a.q + ((int64_t)(q0 + tile_q + (ok_own ? pos_own : 0)) * Hq + kvh * g + m_own % g) * HD + 8 * h;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const u32x4 v = *(const u32x4 *)(qp + s * 32);
-            qb[rt][s] = row_ok[rt] ? v : u32x4{0, 0, 0, 0};
+        for (int s = 0; s < NKS; ++s) {
+            const u32x4 v = *(const u32x4 *)(qp + 16 * s);
+            qb[s] = ok_own ? v : u32x4{0, 0, 0, 0};
         }
     }
 
-    f32x4 acc[kRT][NT];
+    f32x16 acc[ND][kWaves];
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt)
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-            acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[kRT], l_run[kRT];
+        for (int t = 0; t < kWaves; ++t)
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-        m_run[rt] = -INFINITY;
-        l_run[rt] = 0.f;
-    }
+            for (int v = 0; v < 16; ++v)
+                acc[d][t][v] = 0.f;
+    float m_run = -INFINITY, l_part = 0.f;
     int bad_page = 0;
 
-    // ---- page i of the tile's range -> its ring stage, via direct buffer->LDS loads. Lane l
-    // of load k lands at byte (k * kThreads + wave * 64 + l) * 16 of the block; it fetches
-    // the chunk that the swizzled layout puts there. Pages past the range (or with a bad
-    // id) use a zero-size resource: zeros, no traffic.
-    uint32_t src_off[LPB];
-#pragma unroll
-    for (int k = 0; k < LPB; ++k) {
-        const int P = k * kThreads + wave * 64 + lane;  // chunk position in the block
+    // ---- ring fill: load k of a unit writes LDS chunk position P = k*256 + wave*64 + lane,
+    // i.e. token row P / (HD/8), slot P % (HD/8); it fetches the chunk the swizzle puts there.
+    // Loads 0 .. LPU/2-1 cover the block's first page, the rest its second.
+    auto src_off = [&](int k) {
+        const int P = k * kThreads + wave * 64 + lane;
         const int t = P / (HD / 8);
-        const int c = (P % (HD / 8)) ^ (t & 15);
-        src_off[k] = (uint32_t)(t * HD + c * 8) * 2u;
-    }
-    // Page ids of the tile's range, 64 per vector register (lane j: page 64*k + j), read back
-    // with readlane so the page loop never waits on a memory load for an id.
-    auto load_ids = [&](int first) { return pt[pg0 + min(first + lane, max(npg - 1, 0))]; };
-    int ids = load_ids(0), ids_next = load_ids(64);
-    int ids_base = 0;  // page index of ids' lane 0
-    auto issue_page = [&](int i) {
-        int pid = 0;
-        bool live = i < npg;
-        if (live) {
-            const int rel = i - ids_base;  // 0..127
-            pid = __builtin_amdgcn_readlane(rel >= 64 ? ids_next : ids, rel & 63);
-            if (pid < 0 || pid >= a.num_pages) {
-                bad_page = 1;
-                live = false;
-                pid = 0;
-            }
-        }
-        const int64_t blk = ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD);
-        const uint32_t dst = (uint32_t)(uintptr_t)ring[i % NSTAGE] + (uint32_t)(wave * 64 * 16);
-        const u32x4 rk = raw_rsrc(a.k_pool + blk, live ? BLOCK : 0);
-#pragma unroll
-        for (int k = 0; k < LPB; ++k)
-            ring_load16(rk, dst + k * kThreads * 16, src_off[k]);
-        if (!SHARED) {
-            const u32x4 rv = raw_rsrc(a.v_pool + blk, live ? BLOCK : 0);
-#pragma unroll
-            for (int k = 0; k < LPB; ++k)
-                ring_load16(rv, dst + BLOCK + k * kThreads * 16, src_off[k]);
-        }
+        const int c = (P % (HD / 8)) ^ swz(t & 15);
+        return (uint32_t)((t & 15) * HD + c * 8) * 2u;
     };
-
-    // Per-lane LDS byte offsets of the operand reads, K-step / dim-tile 0. The swizzle is an
-    // XOR on bits that the step index does not share with the row base, so step s of the K
-    // read is k_base ^ (64 s) and dim tile j of the V transpose read is v_base ^ (32 j).
-    const uint32_t k_base = (uint32_t)(c16 * HD * 2) + ((uint32_t)(16 * r4) ^ (uint32_t)(16 * c16));
-    const int tok = 4 * r4 + (c16 >> 2), half = (c16 & 3) >> 1;
-    const uint32_t v_base = (uint32_t)(tok * HD * 2) + ((uint32_t)(16 * half) ^ (uint32_t)(16 * tok)) +
-                            8u * (uint32_t)(c16 & 1);
-
-    const float scale = a.scale_log2;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // Q and the first page ids are in registers before the ring starts, so that inside the
-    // page loop the only vector-memory operations in flight are the ring's own loads and the
-    // loop's wait below is exact.
-    __builtin_amdgcn_s_waitcnt(0);  // (the compiler's own view: nothing of its is in flight)
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i)
-        issue_page(i);
-
-    for (int i = 0; i < npg; ++i) {
-        // page i landed for this wave once at most the later NSTAGE-2 pages' loads are
-        // outstanding; the barrier makes every wave's share visible and also certifies that
-        // page i-1's stage has been fully read, so it can be refilled.
-        wait_vmcnt<(NSTAGE - 2) * LPP>();
-        __syncthreads();
-        if (i + NSTAGE - 1 - ids_base >= 64 + 32) {  // slide the id window (every 64 pages)
+    // Page ids of the tile's range, 64 per vector register (lane j: page 64*k + j), read back
+    // with readlane so that the block loop never waits on a memory load for an id.
+    auto load_ids = [&](int first) {
+        return bad_row ? 0 : pt[pgA + min(first + lane, max(npg - 1, 0))];
+    };
+    int ids = load_ids(0), ids_next = load_ids(64);
+    int ids_base = 0;  // page index (relative to pgA) of ids' lane 0
+    // Unit u: block u (K=V) or block u/2, K if u even else V. Units past the last block, and
+    // pages of a block outside [lo, p_last], load zeros with no memory traffic, so that every
+    // wave always has exactly LPU loads per unit in flight and the ring waits stay exact.
+    auto issue = [&](int u) {
+        const int blk = SHARED ? u : (u >> 1);
+        const bool is_v = !SHARED && (u & 1);
+        const uint16_t *pool = is_v ? a.v_pool : a.k_pool;
+        if (blk < nblk && 2 * blk + 1 - ids_base >= 96) {  // slide the id window (every 32 blocks)
             ids = ids_next;
             ids_base += 64;
             ids_next = load_ids(ids_base + 64);
         }
-        issue_page(i + NSTAGE - 1);
-        const uint8_t *kst = ring[i % NSTAGE];
-        const uint8_t *vst = SHARED ? kst : kst + BLOCK;
-
-        // S^T[token c16 .. ][row c16] per row tile: A = K[token c16][8 dims] from LDS (shared by
-        // both tiles), B = Q^T
-        f32x4 st[kRT];
+        u32x4 rs[2];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
-            st[rt] = zero;
-#pragma unroll
-        for (int s0 = 0; s0 < NS; s0 += 2) {
-            // chunk_off(c16, 4s + r4) == k_base ^ (64 s)
-            u32x4 ka[2];
-            k_read2(ka, kst, k_base ^ (64u * s0), 64u);
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-#pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-                    st[rt] = mfma_k32(ka[k], qb[rt][s0 + k], st[rt]);
+        for (int pp = 0; pp < 2; ++pp) {
+            const int rel = 2 * blk + pp;
+            const int pg = pgA + rel;
+            bool live = blk < nblk && pg * kPage <= p_last && pg * kPage + kPage - 1 >= lo;
+            int pid = 0;
+            if (live) {
+                const int r = rel - ids_base;  // 0..127
+                pid = __builtin_amdgcn_readlane(r >= 64 ? ids_next : ids, r & 63);
+                if (pid < 0 || pid >= a.num_pages) {
+                    bad_page = 1;
+                    live = false;
+                    pid = 0;
+                }
+            }
+            rs[pp] = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD), live ? PAGE_BYTES : 0);
         }
-        // mask + online softmax; lane holds S^T[token t0 + 4*r4 + e][row c16 of tile rt]
-        const int t0 = (pg0 + i) * kPage;
-        u32x2 pb[kRT];
+        const uint32_t dst = (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT) + (uint32_t)(wave * 64 * 16);
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 4 * r4 + e;
-                const bool ok = row_ok[rt] && t <= p_row[rt] && t >= lo_row[rt];
-                const float v = ok ? st[rt][e] * scale : -INFINITY;
-                st[rt][e] = v;
-                mx = fmaxf(mx, v);
-            }
-            mx = rows_max(mx);
-            const float m_new = fmaxf(m_run[rt], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with no visible key yet
-            const float alpha = fast_exp2(m_run[rt] - m_use);
-            float ps[4], rs = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ps[e] = fast_exp2(st[rt][e] - m_use);
-                rs += ps[e];
-            }
-            rs = rows_sum(rs);
-            l_run[rt] = l_run[rt] * alpha + rs;
-            m_run[rt] = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[rt][j] *= alpha;
-            }
-            pb[rt] = u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
-        }
+        for (int k = 0; k < LPU; ++k)
+            ring_load16(rs[k < LPU / 2 ? 0 : 1], dst + k * kThreads * 16, src_off(k));
+    };
 
-        // V^T tiles with the transpose read: lane a of 16-lane group r4 supplies 4 dims of
-        // token 4*r4 + a/4; lane c16 receives dim c16 of tokens 4*r4 .. 4*r4+3. Tokens no
-        // row of the tile can see (before the window, past the last query) carry P = 0, and
-        // their V (possibly a NaN slot) is selected out rather than multiplied by zero.
-        const bool edge = t0 < lo || t0 + kPage - 1 > p_last;
-        uint32_t keep[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};
+    // ---- per-lane LDS offsets of the operand reads
+    // K operand (step s): token n32, chunk 2s + h -> n32*HD*2 + 16*((2s + h) ^ swz) =
+    // kb[s & 7] + 256 * (s >> 3), the swizzle touching only the low 8 address bits.
+    uint32_t kb[8];
+    {
+        const int sw = swz(n32 & 15);
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+            kb[v] = (uint32_t)(n32 * HD * 2 + 16 * ((2 * v + h) ^ sw));
+    }
+    // V^T operand (transpose read i of dim tile d, page p): in 16-lane group G (G&1: dims
+    // 16..31 of the tile, G>>1 = h), lane 4r + q supplies token 16p + 8i + 4h + r, dims
+    // 4q .. 4q+3 of its 16; the lane receives its dim for those four tokens.
+    uint32_t vb[2][ND];
+    {
+        const int G = lane >> 4, gh = G & 1, r = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const int tok = 8 * i + 4 * h + r;
+                const int c = (wave * DW) / 8 + 4 * d + 2 * gh + (q >> 1);
+                vb[i][d] = (uint32_t)(tok * HD * 2 + 16 * (c ^ swz(tok)) + 8 * (q & 1));
+            }
+    }
+
+    const float scale = a.scale_log2;
+    // Q and the first page ids are in registers before the ring starts, so that inside the
+    // block loop the only vector-memory operations in flight are the ring's own loads.
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int u = 0; u < NU - 1; ++u)
+        issue(u);
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int uk = SHARED ? blk : 2 * blk;
+        // unit uk landed for this wave once at most the later NU-2 units' loads are
+        // outstanding; the barrier makes every wave's share visible and certifies that the
+        // previous block is fully read, so its slot can be refilled.
+        wait_vmcnt<(NU - 2) * LPU>();
+        __syncthreads();
+        issue(uk + NU - 1);
+        const uint8_t *kst = ring + (uk % NU) * UNIT;
+
+        // ---- S^T[32 tok][32 rows] for this wave's rows. Operand reads run one group of four
+        // K-steps ahead of the MFMAs; the scheduling fences keep the compiler from hoisting
+        // every read of the block (which would not fit beside Q in registers).
+        f32x16 st;
+        auto kread = [&](int s) { return *(const u32x4 *)(kst + kb[s & 7] + 256 * (s >> 3)); };
+        u32x4 kf[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            kf[0][i] = kread(i);
+#pragma unroll
+        for (int j = 0; j < NKS / 4; ++j) {
+            if (j + 1 < NKS / 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    kf[(j + 1) & 1][i] = kread(4 * (j + 1) + i);
+            }
+            const u32x4 *kk = kf[j & 1];
+            if (j == 0)
+                qk4<true>(st, kk[0], kk[1], kk[2], kk[3], qb[0], qb[1], qb[2], qb[3]);
+            else
+                qk4<false>(st, kk[0], kk[1], kk[2], kk[3], qb[4 * j], qb[4 * j + 1], qb[4 * j + 2], qb[4 * j + 3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        qk_settle(st);
+
+        // ---- masked online softmax of the rows; lane holds tokens 8(v/4) + 4h + v%4
+        const int T0 = kb0 + blk * kTok;
+        const bool edge = T0 + kTok - 1 > p_first || (!a.is_global && T0 < p_last - a.window + 1);
+        float mx = -INFINITY;
         if (edge) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 4 * r4 + e;
-                if (t < lo || t > p_last)
-                    keep[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            for (int v = 0; v < 16; ++v) {
+                const int T = T0 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const bool vis = T <= p_own && (a.is_global || p_own - T < a.window);
+                st[v] = vis ? st[v] * scale : -INFINITY;
+                mx = fmaxf(mx, st[v]);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                st[v] *= scale;
+                mx = fmaxf(mx, st[v]);
             }
         }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const bool resc = m_new > m_run + kRescaleLog2;
+        const float alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
+        if (resc)
+            m_run = m_new;
+        const float mb = m_run == -INFINITY ? 0.f : m_run;
+        float ps[16], rs = 0.f;
 #pragma unroll
-        for (int j0 = 0; j0 < NT; j0 += 4) {
-            // chunk_off(tok, 2j + h) + 8 * (c16 & 1) == v_base ^ (32 j)
-            u32x2 vt[4];
-            tr_read4(vt, vst, v_base ^ (32u * j0), 32u);
+        for (int v = 0; v < 16; ++v) {
+            ps[v] = fast_exp2(st[v] - mb);
+            rs += ps[v];
+        }
+        l_part = l_part * alpha + rs;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                u32x2 va = vt[k];
-                va[0] &= keep[0];
-                va[1] &= keep[1];
+        for (int p = 0; p < 2; ++p) {
+            const u32x4 pk = {pack_bf16x2(ps[8 * p + 0], ps[8 * p + 1]), pack_bf16x2(ps[8 * p + 2], ps[8 * p + 3]),
+                              pack_bf16x2(ps[8 * p + 4], ps[8 * p + 5]), pack_bf16x2(ps[8 * p + 6], ps[8 * p + 7])};
+            *(u32x4 *)(p_lds + ((wave * 2 + p) * 64 + lane) * 16) = pk;
+        }
+        const bool any_resc = __builtin_amdgcn_ballot_w64(resc) != 0;
+        if (h == 0)
+            alpha_lds[m_own] = alpha;
+        if (lane == 0)
+            flag_lds[wave] = any_resc;
+
+        // ---- V unit (separate pools) and the P exchange
+        const int uv = SHARED ? blk : 2 * blk + 1;
+        if (!SHARED)
+            wait_vmcnt<(NU - 2) * LPU>();
+        __syncthreads();
+        if (!SHARED)
+            issue(uv + NU - 1);
+        const uint8_t *vst = ring + (uv % NU) * UNIT;
+
 #pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-                    acc[rt][j0 + k] = mfma_k16(va, pb[rt], acc[rt][j0 + k]);
+        for (int t = 0; t < kWaves; ++t) {
+            if (__builtin_amdgcn_readfirstlane(flag_lds[t])) {
+                const float al = alpha_lds[32 * t + n32];
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    scale_acc(acc[d][t], al);
+            }
+        }
+        // Tokens no row of the tile can see (before the window, past the last query) carry
+        // P = 0; their V (possibly a never-written slot) is selected out rather than
+        // multiplied by zero.
+        u32x2 keep[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                keep[p][i] = u32x2{0xFFFFFFFFu, 0xFFFFFFFFu};
+                if (edge) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int T = T0 + 16 * p + 8 * i + 4 * ((lane >> 5) & 1) + r;
+                        if (T < lo || T > p_last)
+                            keep[p][i][r >> 1] &= (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                    }
+                }
+            }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            u32x4 pf[kWaves];
+#pragma unroll
+            for (int t = 0; t < kWaves; ++t)
+                pf[t] = *(const u32x4 *)(p_lds + ((t * 2 + p) * 64 + lane) * 16);
+            auto vread = [&](int d) {
+                u32x2 v0 = tr_read(vst + vb[0][d] + p * PAGE_BYTES);
+                u32x2 v1 = tr_read(vst + vb[1][d] + p * PAGE_BYTES);
+                return u32x4{v0[0], v0[1], v1[0], v1[1]};
+            };
+            u32x4 vf[2];
+            vf[0] = vread(0);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                if (d + 1 < ND)
+                    vf[(d + 1) & 1] = vread(d + 1);
+                u32x4 va = vf[d & 1];
+                if (edge)
+                    va &= u32x4{keep[p][0][0], keep[p][0][1], keep[p][1][0], keep[p][1][1]};
+#pragma unroll
+                for (int t = 0; t < kWaves; ++t)
+                    acc[d][t] = mfma32(va, pf[t], acc[d][t]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    // ---- normalise and write this wave's rows
+    // No ring load (the zero-filling ones past the last block included) may still be writing
+    // this workgroup's LDS when it ends.
+    wait_vmcnt<0>();
+
+    // ---- row sums, LSE (score owners), then normalise and write O (dim owners)
     const bool bad = bad_row || __builtin_amdgcn_ballot_w64(bad_page) != 0;
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-        if (!row_ok[rt])
-            continue;
-        const int64_t orow = (int64_t)(q0 + tile_q + row_pos[rt]) * Hq + kvh * g + row_head[rt];
-        const float inv = 1.0f / l_run[rt];
-        uint16_t *op = a.out + orow * HD + 4 * r4;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            f32x4 o = acc[rt][j] * inv;
-            if (bad)
-                o = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-            *(u32x2 *)(op + 16 * j) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    if (h == 0) {
+        l_lds[m_own] = l_tot;
+        if (ok_own) {
+            const int64_t orow = (int64_t)(q0 + tile_q + pos_own) * Hq + kvh * g + m_own % g;
+            a.lse[orow] = bad ? __builtin_nanf("") : (m_run + fast_log2(l_tot)) * kLn2;
         }
-        if (r4 == 0)
-            a.lse[orow] = bad ? __builtin_nanf("") : (m_run[rt] + fast_log2(l_run[rt])) * kLn2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kWaves; ++t) {
+        const int m = 32 * t + n32;
+        const int pos = m / g;
+        if (pos >= nq)
+            continue;
+        const float inv = 1.0f / l_lds[m];
+        const int64_t orow = (int64_t)(q0 + tile_q + pos) * Hq + kvh * g + m % g;
+        uint16_t *op = a.out + orow * HD + wave * DW + 4 * h;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = bad ? __builtin_nanf("") : acc[d][t][4 * j + e] * inv;
+                *(u32x2 *)(op + 32 * d + 8 * j) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            }
     }
 }
 
 template <int HD, bool SHARED>
 hipError_t launch(const PrefillArgs &a, dim3 grid, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(Shape<HD>::THREADS), args, 0,
-                           stream);
+    return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, bool kv_shared, int batch, hipStream_t stream) {
-    const int bq = (head_dim == 256 ? Shape<256>::ROWS : Shape<512>::ROWS) / a.group;
+    const int bq = kRows / a.group;
     const dim3 grid((a.max_q + bq - 1) / bq, a.num_kv_heads, batch);
     if (head_dim == 256)
         return kv_shared ? launch<256, true>(a, grid, stream) : launch<256, false>(a, grid, stream);
