@@ -33,6 +33,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the local decode, 60-layer sweep and long run")
     p.add_argument("--no-flushed", action="store_true",
                    help="skip the MALL-flushed re-measurement (profiling runs: keeps every decode launch "
                         "in the kernel trace identical to the timed ones)")
@@ -122,6 +123,109 @@ def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
                     "workload": f"{fam}: 4 chunks x 2048 queries, priors {pre.ctx_lens.tolist()}"}
         del d
     return out
+
+
+def event_times(torch, stream, fn, n, flush=None):
+    """Per-call durations (s) of ``fn`` from HIP events recorded on ``stream``; with ``flush``, a
+    1 GiB buffer is overwritten before each call, outside the events."""
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        if flush is not None:
+            torch.cuda.synchronize()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in ts]
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def local_decode_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
+    """The local-family decode workload (batch 64, hd 256, 16 KV heads, window 1024, contexts
+    ~U{512..32768}, window pages only, split 512), pools filled on the device."""
+    lay = workloads.paged_layout(workloads.LOCAL_31B, workloads.ragged((3, 0), 512, 32768, 64), (3, 0))
+    d = devio.DeviceLayout(lay, workloads.fill_normal_bf16_device)
+    s = lay.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, lay.ctx_lens)
+    for _ in range(5):
+        d.decode(512)
+    t = median(event_times(torch, stream, lambda: d.decode(512), steps))
+    tf = median(event_times(torch, stream, lambda: d.decode(512), 10, flush))
+    return {"workload": "local decode: batch 64, 32 q heads, 16 KV heads, hd 256, window 1024, contexts "
+                        "~U{512..32768}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
+            "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
+            "mall_flushed_gbs": round(kv / tf / 1e9, 1)}
+
+
+def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
+    """The 60-layer decode sweep (5 local : 1 global, last global; 16 rows at 32768 tokens; global
+    layers K=V with 1024-token splits, local layers 512) with every layer's pools resident, timed
+    end to end and per family; then the 65536-token global K=V decode."""
+    nat = devio.nat
+    n = workloads.SWEEP_LAYERS
+    layers, kv_total, kv_fam = [], 0, {"local": 0, "global": 0}
+    for l in range(n):
+        fam = "global" if nat.gattn_layer_family(l, n) == nat.GLOBAL else "local"
+        lay = workloads.sweep_layer(l, fam)
+        s = lay.spec
+        kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, lay.ctx_lens)
+        kv_total += kv
+        kv_fam[fam] += kv
+        layers.append((fam, devio.DeviceLayout(lay, workloads.fill_normal_bf16_device)))
+    ws_bytes = max(d.workspace_bytes(workloads.SWEEP_SPLIT[f]) for f, d in layers)
+    ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
+    for _, d in layers:
+        d.workspace, d.ws_bytes = ws, ws_bytes
+
+    def sweep():
+        for fam, d in layers:
+            d.decode(workloads.SWEEP_SPLIT[fam])
+
+    sweep()
+    torch.cuda.synchronize()
+    t = median(event_times(torch, stream, sweep, reps))
+    # per layer: events around every call of one more sweep
+    evs = []
+    for fam, d in layers:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        d.decode(workloads.SWEEP_SPLIT[fam])
+        e1.record(stream)
+        evs.append((fam, e0, e1))
+    torch.cuda.synchronize()
+    per = {"local": 0.0, "global": 0.0}
+    for fam, e0, e1 in evs:
+        per[fam] += e0.elapsed_time(e1) * 1e-3
+    out = {"workload": "60-layer decode sweep (LLLLLG x10), 16 rows x 32768 tokens; global: hd 512, 4 KV "
+                       "heads, K=V, split 1024; local: hd 256, 16 KV heads, window 1024, split 512",
+           "kv_bytes": kv_total, "ms": round(t * 1e3, 4), "gbs": round(kv_total / t / 1e9, 1),
+           "frac": round(kv_total / t / 1e9 / HBM_PEAK_GBS, 4)}
+    for fam in ("local", "global"):
+        out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
+        out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
+    del layers, ws
+    torch.cuda.empty_cache()
+
+    lay = workloads.long_global_decode(rows=())
+    d = devio.DeviceLayout(lay, workloads.fill_normal_bf16_device)
+    s = lay.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, lay.ctx_lens)
+    for _ in range(5):
+        d.decode(1024)
+    tl = median(event_times(torch, stream, lambda: d.decode(1024), 50))
+    tlf = median(event_times(torch, stream, lambda: d.decode(1024), 10, flush))
+    long = {"workload": "one 65536-token global decode row, K=V, split 1024", "kv_bytes": kv,
+            "us": round(tl * 1e6, 2), "gbs": round(kv / tl / 1e9, 1),
+            "mall_flushed_us": round(tlf * 1e6, 2), "mall_flushed_gbs": round(kv / tlf / 1e9, 1)}
+    return out, long
 
 
 def main():
@@ -228,6 +332,12 @@ def main():
             result["prefill"] = prefill_measure(torch, devio, workloads, traffic, flush)
         except Exception as e:  # report, never hide
             result["prefill"] = {"error": str(e)[:200]}
+    if not args.no_sweep:
+        try:
+            result["local_decode"] = local_decode_measure(torch, devio, workloads, traffic, stream, flush)
+            result["sweep"], result["long_decode"] = sweep_measure(torch, devio, workloads, traffic, stream, flush)
+        except Exception as e:  # report, never hide
+            result["sweep"] = {"error": str(e)[:300]}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(batch, kv_bytes)
     print(json.dumps(result), flush=True)

@@ -85,3 +85,61 @@ def prefill(batch, max_q=None):
     d = DeviceBatch(batch)
     d.prefill(max_q)
     return d.result()
+
+
+class DeviceLayout:
+    """A full-size paged decode layout (workloads.PagedLayout) resident on the GPU.
+
+    Pools are filled on the device by ``fill(tensor, seed)``; the host-drawn rows' pages are then
+    scattered in with torch indexing (page-major blocks from the token-major host rows). The
+    workspace may be shared between layouts that run one after another on one stream.
+    """
+
+    def __init__(self, lay, fill, workspace=None):
+        s = lay.spec
+        self.lay = lay
+        self.layer = layer_of(s)
+        shape = (lay.num_pages, s.num_kv_heads, s.page_size, s.head_dim)
+        self.k_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
+        fill(self.k_pool, lay.fill_seed)
+        self.v_pool = None
+        if not s.kv_shared:
+            self.v_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
+            fill(self.v_pool, lay.fill_seed + 1)
+        for r in lay.rows:
+            pids = torch.from_numpy(lay.row_pages[r]).to("cuda")
+            for pool, tok in ((self.k_pool, lay.k_tok.get(r)), (self.v_pool, lay.v_tok.get(r))):
+                if pool is None or tok is None:
+                    continue
+                t = dev(tok).view(len(lay.row_pages[r]), s.page_size, s.num_kv_heads, s.head_dim)
+                pool[pids] = t.permute(0, 2, 1, 3).contiguous()
+        self.q = dev(lay.q)
+        self.page_table = dev(lay.page_table.astype(np.int32))
+        self.ctx_lens = dev(lay.ctx_lens.astype(np.int32))
+        self.out = torch.empty((lay.B, s.num_q_heads, s.head_dim), dtype=torch.int16, device="cuda")
+        self.lse = torch.empty((lay.B, s.num_q_heads), dtype=torch.float32, device="cuda")
+        self.workspace = workspace
+        self.ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+    def workspace_bytes(self, split_tokens, max_ctx=None):
+        max_ctx = int(self.lay.ctx_lens.max()) if max_ctx is None else int(max_ctx)
+        return nat.gattn_decode_workspace_bytes(self.layer, self.lay.B, max_ctx, split_tokens)
+
+    def decode(self, split_tokens, max_ctx=None, stream=None):
+        lay = self.lay
+        max_ctx = int(lay.ctx_lens.max()) if max_ctx is None else int(max_ctx)
+        need = self.workspace_bytes(split_tokens, max_ctx)
+        if need > self.ws_bytes:
+            self.workspace = torch.empty(need // 4, dtype=torch.float32, device="cuda")
+            self.ws_bytes = need
+        nat.gattn_decode(self.layer, self.q, self.k_pool, self.v_pool, lay.num_pages, self.page_table,
+                         lay.pt_stride, self.ctx_lens, lay.B, max_ctx, split_tokens, self.workspace, self.ws_bytes,
+                         self.out, self.lse, stream)
+
+    def result(self, rows=None):
+        torch.cuda.synchronize()
+        o = host_bf16(self.out).astype(np.float64)
+        l = self.lse.cpu().numpy().astype(np.float64)
+        if rows is not None:
+            o, l = o[list(rows)], l[list(rows)]
+        return o, l

@@ -56,13 +56,31 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def normal_bf16(gen: np.random.Generator, shape) -> np.ndarray:
-    """bf16 bits of N(0,1) draws: float64 -> float32 (RNE) -> bfloat16 (RNE)."""
+    """bf16 bits of N(0,1) draws: float64 -> float32 (RNE) -> bfloat16 (RNE).
+
+    The draws go through fixed chunk buffers that are reused (fresh allocations per
+    chunk are dominated by page faults); the values equal f32_to_bf16_bits applied to
+    ``gen.standard_normal(n).astype(np.float32)``.
+    """
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.uint16)
-    chunk = 1 << 24
+    chunk = max(1, min(n, 1 << 22))
+    f64 = np.empty(chunk, np.float64)
+    f32 = np.empty(chunk, np.float32)
+    u = f32.view(np.uint32)
+    t = np.empty(chunk, np.uint32)
     for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = f32_to_bf16_bits(gen.standard_normal(e - s).astype(np.float32))
+        m = min(n, s + chunk) - s
+        gen.standard_normal(out=f64[:m])
+        f32[:m] = f64[:m]
+        tm = t[:m]
+        # round to nearest even on the float32 bits: add 0x7FFF + (bit 16), keep the high half
+        np.right_shift(u[:m], np.uint32(16), out=tm)
+        np.bitwise_and(tm, np.uint32(1), out=tm)
+        np.add(tm, np.uint32(0x7FFF), out=tm)
+        np.add(tm, u[:m], out=tm)
+        np.right_shift(tm, np.uint32(16), out=tm)
+        out[s:s + m] = tm
     return out.reshape(shape)
 
 
@@ -309,3 +327,110 @@ def permute_pages(batch: Batch, key, extra_pages: int = 0, fill=0) -> Batch:
     out = replace(batch, page_table=pt, k_pool=k_pool, v_pool=v_pool)
     out.meta = dict(batch.meta, repaged=tuple(key))
     return out
+
+
+# --------------------------------------------------------------------------- full-size layouts
+SWEEP_LAYERS, SWEEP_B, SWEEP_L = 60, 16, 32768
+SWEEP_SPLIT = {"local": 512, "global": 1024}
+LONG_L = 65536
+
+
+@dataclass
+class PagedLayout:
+    """One layer's paged batch at full size, with K/V values drawn on the host only for some rows.
+
+    Every row gets its context length, its backed pages (a global seeded shuffle of page ids, as
+    in ``make_batch``) and its queries. The K/V values of the rows in ``rows`` come from the host
+    generator (one PCG64 stream per row and tensor), and ``host`` holds them contiguously for the
+    oracle. The other rows' pages are meant to be filled on the device with
+    ``fill_normal_bf16_device`` from ``fill_seed``: they load the call at its real size, and rows
+    are independent, so the sampled rows' outputs do not depend on those values.
+    """
+    spec: LayerSpec
+    ctx_lens: np.ndarray        # int32 [B]
+    k_starts: np.ndarray        # int32 [B]: first backed token of each row (page-aligned down)
+    page_table: np.ndarray      # int32 [B][pt_stride]
+    num_pages: int
+    q: np.ndarray               # uint16 [B][Hq][hd]
+    rows: tuple                 # rows drawn on the host
+    row_pages: dict             # r -> int64 physical page ids of row r's backed pages, in order
+    k_tok: dict                 # r -> uint16 [n_pg * P][Hkv][hd]: every slot of row r's backed
+                                #      pages, token-major from token k_starts[r]
+    v_tok: dict                 # same for V (empty when K=V)
+    host: Optional[Batch]       # contiguous side of the sampled rows (None when rows is empty)
+    fill_seed: int
+
+    @property
+    def B(self) -> int:
+        return int(self.ctx_lens.shape[0])
+
+    @property
+    def pt_stride(self) -> int:
+        return int(self.page_table.shape[1])
+
+
+def paged_layout(spec: LayerSpec, ctx_lens, key, rows=(), pt_stride: Optional[int] = None) -> PagedLayout:
+    """Decode layout (one query per row) for ``spec``: global rows back every page up to L,
+    local rows only the pages that hold a visible key (the rest of the table is -1)."""
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    B, P = int(ctx_lens.shape[0]), spec.page_size
+    Hkv, hd, Hq = spec.num_kv_heads, spec.head_dim, spec.num_q_heads
+    need = np.array([first_needed_token(spec, int(L), 1) for L in ctx_lens], np.int64)
+    first_pg = need // P
+    last_pg = (ctx_lens.astype(np.int64) - 1) // P
+    n_pg = last_pg - first_pg + 1
+    total = int(n_pg.sum())
+    if pt_stride is None:
+        pt_stride = int((ctx_lens.max() + P - 1) // P)
+    ids = generator(*key, T_PERM).permutation(total)
+    page_table = np.full((B, pt_stride), -1, dtype=np.int32)
+    row_pages, pos = {}, 0
+    for r in range(B):
+        page_table[r, first_pg[r]:last_pg[r] + 1] = ids[pos:pos + n_pg[r]]
+        row_pages[r] = ids[pos:pos + n_pg[r]].astype(np.int64)
+        pos += int(n_pg[r])
+    q = normal_bf16(generator(*key, T_Q), (B, Hq, hd))
+    rows = tuple(int(r) for r in rows)
+    k_tok, v_tok, ks, vs = {}, {}, [], []
+    for r in rows:
+        nt = int(n_pg[r]) * P
+        lo_keep, hi_keep = int(need[r] - first_pg[r] * P), int(ctx_lens[r] - first_pg[r] * P)
+        k_tok[r] = normal_bf16(generator(*key, r, T_K), (nt, Hkv, hd))
+        ks.append(k_tok[r][lo_keep:hi_keep])
+        if not spec.kv_shared:
+            v_tok[r] = normal_bf16(generator(*key, r, T_V), (nt, Hkv, hd))
+            vs.append(v_tok[r][lo_keep:hi_keep])
+    host = None
+    if rows:
+        sel = list(rows)
+        cat = (lambda xs: xs[0] if len(xs) == 1 else np.concatenate(xs))
+        empty = np.zeros((0, Hkv, P, hd), np.uint16)
+        host = Batch(spec, ctx_lens[sel].copy(), np.ones(len(sel), np.int32), need[sel].astype(np.int32),
+                     q[sel].copy(), cat(ks), None if spec.kv_shared else cat(vs),
+                     page_table[sel].copy(), empty, None, {"key": tuple(key), "rows": rows})
+    fill_seed = int(generator(*key, T_PRIOR + 1).integers(1, 2 ** 62))
+    return PagedLayout(spec, ctx_lens, (first_pg * P).astype(np.int32), page_table, total, q, rows,
+                       row_pages, k_tok, v_tok, host, fill_seed)
+
+
+def fill_normal_bf16_device(t, seed: int, chunk: int = 1 << 26) -> None:
+    """Fill a device tensor (bf16, or int16 holding bf16 bits) with N(0,1) values rounded to
+    bf16, drawn by torch's device generator from ``seed``."""
+    import torch
+    flat = t.view(torch.bfloat16).view(-1) if t.dtype == torch.int16 else t.view(-1)
+    g = torch.Generator(device=t.device)
+    g.manual_seed(int(seed))
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        flat[s:e] = torch.randn(e - s, generator=g, device=t.device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def sweep_layer(layer: int, family: str, rows=()) -> PagedLayout:
+    """Layer ``layer`` of the 60-layer decode sweep: 16 rows at 32768 tokens; global layers share
+    K and V (head_dim 512, 4 KV heads), local layers are the 31B local family (window pages only)."""
+    return paged_layout(cfg5_layer_spec(family), np.full(SWEEP_B, SWEEP_L, np.int32), (5, layer), rows)
+
+
+def long_global_decode(rows=(0,)) -> PagedLayout:
+    """One 65536-token global decode row with K=V (split 1024 in the sweep's global setting)."""
+    return paged_layout(GLOBAL_31B_KV_SHARED, np.array([LONG_L], np.int32), (5, SWEEP_LAYERS), rows)
