@@ -13,10 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
 SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip"]
-# MFMA results and accumulators in VGPRs (AGPRs then serve as spill space): the decode
-# kernels otherwise keep copies of the accumulator in both register files. (The prefill
-# kernel keeps its output accumulators in AGPRs.)
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra hipcc flags (none at present: the kernels keep their MFMA accumulators
+# in AGPRs, which leaves the VGPRs to operand prefetch).
+EXTRA = {}
 ARCH = "gfx950"
 
 

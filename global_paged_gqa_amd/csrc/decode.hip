@@ -9,23 +9,28 @@
 // tile pruning that page 5's "Three load-bearing facts" #1 credits with a 3-4x
 // gain).
 //
-// Work split inside the workgroup (four waves): a wave owns 256 head dims of
-// the pages of its page group. With head_dim 256 there are four page groups of
-// one wave each; with head_dim 512 there are two groups of two waves, the pair
-// splitting the head dims and adding their partial scores through LDS (one
-// barrier per page). Each group keeps its own online-softmax state for the g
-// query heads sharing this KV head; the groups merge at the end through LDS in
-// a fixed order, so results are bitwise independent of the batch.
+// Memory path. Decode reads every visible K/V byte exactly once, so it is bound by
+// HBM bandwidth. Each page's (page, KV head) block is contiguous in the pool, and it
+// is copied global -> LDS with 16-byte-per-lane buffer loads that read 1 KB of
+// consecutive bytes per instruction (reading 16 token rows x 64 B per instruction
+// straight into MFMA operand registers caps the same gather well below the
+// contiguous rate). The loads are non-temporal (every byte is read once) and go
+// straight to LDS, holding no registers.
 //
-// Per page (16 tokens) a wave does, in registers:
-//   S^T[16 tok][16 heads] = K[16 tok][dims] . Q^T[dims][16 heads]   (MFMA 16x16x32, bf16)
-//   online softmax on S^T columns                                     (VALU + lane shuffles)
-//   V^T tile = MFMA(V, identity)  -- an exact register transpose of V
-//   O^T[dims][16 heads] += V^T[dims][16 tok] . P^T[16 tok][16 heads]  (MFMA 16x16x16, bf16)
-// K/V are read 16 B per lane straight from the page into the MFMA operand layout
-// (each instruction reads 64 contiguous bytes of 16 token rows), one page ahead
-// of the math, through buffer loads whose resource has zero size past the end of
-// the wave's page list (no traffic, no fault, no conditional load).
+// Work split. The W waves of a workgroup (W = 1 for head_dim 512, 2 for 256) run
+// independently: wave w takes pages w, w+W, w+2W, ... of the split, streams them through
+// its own slice of LDS (two or three K/V units ahead of the math, waited for with explicit
+// per-wave load counts, no barriers) and keeps its own online-softmax state over the whole
+// head dimension. Per page (16 tokens), in registers:
+//   S^T[16 tok][16 heads] = K[tok][:] . Q^T[:][heads]    (MFMA 16x16x32, A = K read
+//                                                         from LDS, B = Q^T in registers)
+//   online softmax on S^T columns                         (VALU, lane swaps)
+//   O^T[dims][heads] += V^T[dims][tok] . P^T[tok][heads]  (MFMA 16x16x16, A = V^T from
+//                        the gfx950 transpose read of the page, B = P^T straight from the
+//                        score tile's accumulator layout)
+// The g query heads sharing the KV head fill the 16 MFMA columns (padding heads have
+// zero queries and are never written). At the end the wave states merge through LDS in a
+// fixed order, so the result does not depend on timing or on the batch.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,35 +38,69 @@ namespace gattn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kDimsPerWave = 256;
-constexpr int kMergeBytes = 32 * 1024;
-constexpr int kOcc = 2;  // workgroups per CU the register budget is sized for
 
-struct PageRegs {
-    u32x4 r[kDimsPerWave / 32];
-};
+// LDS layout of one unit (one page's K or V for one KV head: 16 token rows of HD bf16):
+// token row t at t * HD * 2 bytes, its 16-byte chunk c at chunk slot c ^ dswz(t). dswz is a
+// bijection of the four token bits whose values for tokens 0..7 (and for 8..15) differ above
+// bit 0, so that (i) a K operand read (16 tokens at one chunk) hits 16 different 16-byte bank
+// groups and (ii) a transpose read of a 16-dim tile (8 tokens x 2 adjacent chunks in each half
+// wave) hits 16. Token rows are multiples of 256 bytes, so only the chunk slot picks the bank.
+__device__ __forceinline__ int dswz(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
 
-template <int HD, bool SHARED, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(DecodeArgs a) {
-    constexpr int DS = HD / kDimsPerWave;      // waves sharing one page (1 or 2)
-    constexpr int NGRP = kWaves / DS;          // page groups
-    constexpr int NS = kDimsPerWave / 32;      // K-steps of 32 dims for QK, per wave
-    constexpr int NT = kDimsPerWave / 16;      // 16-dim output tiles, per wave
-    constexpr int kQStride = HD + 8;           // padded LDS row (bf16 elements) of one head's query
-    constexpr int kChunk = kMergeBytes / 4 / (NGRP * HD);  // heads merged per round
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane swaps. v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0
+// and 2 of its second; with both operands holding x, each lane ends up with its own value in
+// one register and its row partner's (lane l^16) in the other. v_permlane32_swap does the same
+// for lanes l and l^32. Written as assembly: given two copies of one value, the compiler folds
+// the builtins' two results into one. Both reductions are symmetric, so all four lanes of a
+// column get the identical value.
+__device__ __forceinline__ void swap_rows16(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_halves32(float &a, float &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 
-    __shared__ float sm_o[kMergeBytes / 4];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_q[16 * kQStride];
-    __shared__ f32x4 sm_s[DS > 1 ? 2 : 1][DS > 1 ? kWaves * 64 : 1];  // partial scores, double-buffered
-    __shared__ float sm_m[NGRP][16];
-    __shared__ float sm_l[NGRP][16];
-    __shared__ int sm_bad[kWaves];
+__device__ __forceinline__ float rows_max4(float x) {
+    float a = x, b = x;
+    swap_rows16(a, b);
+    float c = fmaxf(a, b), d = c;
+    swap_halves32(c, d);
+    return fmaxf(c, d);
+}
+
+__device__ __forceinline__ float rows_sum4(float x) {
+    float a = x, b = x;
+    swap_rows16(a, b);
+    float c = a + b, d = c;
+    swap_halves32(c, d);
+    return c + d;
+}
+
+template <int HD, bool SHARED, int W, int kSliceBytes>
+__global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
+    // W waves, each an independent page stream through its own kSliceBytes of LDS
+    constexpr int kThreads = W * 64;
+    constexpr int kRingBytes = W * kSliceBytes;
+    constexpr int NKS = HD / 32;                 // K-steps of 32 dims in the score product
+    constexpr int NDT = HD / 16;                 // 16-dim output tiles in the PV product
+    constexpr int UNIT = kPage * HD * 2;         // bytes of one page's K (or V), one KV head
+    constexpr int UPP = SHARED ? 1 : 2;          // units per page
+    constexpr int SUB = kSliceBytes;
+    constexpr int NU = SUB / UNIT;               // units in a slice
+    constexpr int LPU = UNIT / 1024;             // 1 KB load instructions per unit
+    constexpr int CPR = HD / 8;                  // 16-byte chunks per token row
+    static_assert(NU >= 2, "decode ring shape");
+    static_assert(NU * LPU + 1 <= 63, "vmcnt range");
+    static_assert(16 * HD * 4 <= kSliceBytes, "merge buffer");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
+    __shared__ float sm_m[W][16];
+    __shared__ float sm_l[W][16];
+    __shared__ int sm_bad[W];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int grp = wave / DS, dpart = wave % DS;
     const int c16 = lane & 15;  // MFMA row/column index of this lane
     const int r4 = lane >> 4;   // 16-lane row of this lane
     const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -86,272 +125,263 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_split_kernel(DecodeArgs 
             a.lse_part[((int64_t)b * Hq + kvh * g + threadIdx.x) * a.n_slots + slot] = -INFINITY;
         return;
     }
-
-    const int pg0 = tb / kPage, pg1 = (te - 1) / kPage;
-    const int npg = bad_len ? 0 : pg1 - pg0 + 1;
-    const int cnt = npg > grp ? (npg - grp + NGRP - 1) / NGRP : 0;  // pages of this group
-    const int cnt_max = (npg + NGRP - 1) / NGRP;                       // of the largest group
-    // Paired waves meet at a barrier every page, so every wave runs the same trip count.
-    const int trips = DS > 1 ? cnt_max : cnt;
-
-    const int64_t blk = (int64_t)kPage * HD;  // elements of one (page, KV head) block
-    const uint32_t lane_off = (uint32_t)(c16 * HD + dpart * kDimsPerWave + r4 * 8) * 2u;  // bytes
+    const int pg0 = tb / kPage;
+    const int npg = bad_len ? 0 : (te - 1) / kPage - pg0 + 1;
+    const int my_pages = npg > wave ? (npg - wave + W - 1) / W : 0;  // this wave's: w, w+W, ...
     const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
-    const int pg_hi = npg > 0 ? pg1 : 0;  // last page-table entry this workgroup may read
-    auto page_of = [&](int i) { return pg0 + grp + NGRP * i; };
+    const int pg_hi = npg > 0 ? pg0 + npg - 1 : pg0;  // last table entry this workgroup may read
 
-    // ---- page ids, 64 at a time in one vector register: lane j holds the id of the group's
-    // page 64*k + j. Pages read their id back with readlane, so no page waits on a scalar
-    // load; the next 64 ids are fetched one block ahead. Out-of-range indices are clamped to
-    // an entry the workgroup owns (their ids are never used).
-    auto load_ids = [&](int first) { return pt[min(page_of(first + lane), pg_hi)]; };
-    int ids = load_ids(0);
-    int ids_next = load_ids(64);
+    // ---- this wave's page ids, 64 at a time in one vector register (lane j: the wave's page
+    // 64k + j), read back with readlane when a page is issued. Indices past the split are
+    // clamped to an entry the workgroup owns (their ids are never used).
+    auto load_ids = [&](int first) { return pt[min(pg0 + (first + lane) * W + wave, pg_hi)]; };
+    int ids = load_ids(0), ids_next = load_ids(64);
+    int ids_base = 0;
 
-    // ---- Q^T as the B operand, staged once in LDS for the 16 MFMA columns (the g real
-    // heads, zeros for the rest); each page reads lane's head c16, 8 dims per K-step.
-    constexpr int kQItems = 16 * (HD / 8) / kThreads;
-    u32x4 qv[kQItems];
+    // ---- Q^T as the B operand of the score product: lane holds head c16 (zeros past g),
+    // dims 32 s + 8 r4 .. +7
+    u32x4 qb[NKS];
+    {
+        const uint16_t *qp = a.q + ((int64_t)b * Hq + kvh * g + min(c16, g - 1)) * HD + 8 * r4;
 #pragma unroll
-    for (int k = 0; k < kQItems; ++k) {
-        const int e = threadIdx.x + k * kThreads;
-        const int hn = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-        // unconditional load of a valid head, zeroed afterwards for the padding columns
-        const u32x4 v = *(const u32x4 *)(a.q + ((int64_t)b * Hq + kvh * g + min(hn, g - 1)) * HD + d8);
-        qv[k] = hn < g ? v : u32x4{0, 0, 0, 0};
-    }
-    const uint16_t *q_lane = sm_q + c16 * kQStride + dpart * kDimsPerWave + r4 * 8;
-    // Identity blocks for the register transpose: B[(r4, e)][c16] = 1 iff 8*r4 + e == 16*h + c16.
-    u32x4 ident[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int e = 2 * e2;
-            uint32_t lo = (8 * r4 + e == 16 * h + c16) ? 0x3F80u : 0u;
-            uint32_t hi = (8 * r4 + e + 1 == 16 * h + c16) ? 0x3F80u : 0u;
-            w[e2] = lo | (hi << 16);
+        for (int s = 0; s < NKS; ++s) {
+            const u32x4 v = *(const u32x4 *)(qp + 32 * s);
+            qb[s] = c16 < g ? v : u32x4{0, 0, 0, 0};
         }
-        ident[h] = u32x4{w[0], w[1], w[2], w[3]};
     }
 
-    f32x4 acc[NT];
+    // ---- per-lane LDS byte offsets. The swizzle only permutes the low four bits of a chunk
+    // index, so operand offsets repeat with a period of 16 chunks (256 bytes) and the rest of
+    // each offset is an immediate.
+    // K operand (step s): token c16, logical chunk 4 s + r4 -> kbase[s % 4] + 256 (s / 4)
+    uint32_t kbase[4];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+        kbase[j] = (uint32_t)(c16 * HD * 2 + ((4 * j + r4) ^ dswz(c16)) * 16);
+    // V^T operand (dim tile dt): in 16-lane group r4, lane 4r + q supplies token 4 r4 + r,
+    // dims 16 dt + 4q .. +3; the lane receives dim 16 dt + c16 of those four tokens.
+    // -> vbase[dt % 8] + 256 (dt / 8)
+    uint32_t vbase[8];
+    {
+        const int t = 4 * r4 + (c16 >> 2), q = c16 & 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            vbase[j] = (uint32_t)(t * HD * 2 + ((2 * j + (q >> 1)) ^ dswz(t)) * 16 + 8 * (q & 1));
+    }
+    // ring fill: instruction i of a unit writes lane's 16 bytes to the slice's chunk position
+    // P = 64 i + lane, which holds token P / CPR at chunk slot P % CPR, i.e. that token's chunk
+    // (slot ^ dswz(token)) of the page block.
+    auto src_off = [&](int i) {
+        const int P = 64 * i + lane;
+        const int t = P / CPR;
+        return (uint32_t)(t * CPR + ((P % CPR) ^ dswz(t))) * 16u;
+    };
+
+    f32x4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     int bad_page = 0;
+    uint8_t *const sub = ring + wave * SUB;
+    const uint32_t sub_lds = (uint32_t)(uintptr_t)sub;
 
-    // Buffer resource of this KV head's block in page i of the group's list. Past the end of
-    // the list, or for a page id outside the pool, the resource has zero size: its loads
-    // return zeros without touching memory, so every load can be issued unconditionally
-    // (which keeps the compiler's wait counts exact across the software pipeline).
-    auto page_rsrc = [&](const uint16_t *pool, int i, int ib) {
-        const int rel = i - ib;  // 0..65: position in ids (or, past 63, in ids_next)
-        int pid = __builtin_amdgcn_readlane(rel >= 64 ? ids_next : ids, rel & 63);
-        bool live = i < cnt;
+    // Issue unit u of this wave's stream (its page u / UPP; K, or V when u is odd and the
+    // pools are separate) into slice slot u % NU. Pages past the wave's share, and page ids
+    // outside the pool, get a zero-size buffer resource: their loads write zeros and touch no
+    // memory, so the wave always has exactly LPU loads per unit in flight and the waits below
+    // stay exact. The slot's previous unit has been read: its LDS reads are waited for first.
+    auto issue = [&](int u) {
+        const int k = u / UPP;
+        if (k - ids_base >= 64) {  // slide the id window
+            ids = ids_next;
+            ids_base += 64;
+            ids_next = load_ids(ids_base + 64);
+        }
+        int pid = __builtin_amdgcn_readlane(ids, k - ids_base);
+        bool live = k < my_pages;
         if (live && (pid < 0 || pid >= a.num_pages)) {
             bad_page = 1;
             live = false;
         }
         if (!live)
             pid = 0;
-        const uint16_t *base = pool + ((int64_t)pid * a.num_kv_heads + kvh) * blk;
-        return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, live ? (int)(blk * 2) : 0, 0x00020000);
-    };
-    auto load_regs = [&](PageRegs &R, __amdgpu_buffer_rsrc_t rsrc) {
+        const uint16_t *pool = (SHARED || (u & 1) == 0) ? a.k_pool : a.v_pool;
+        const u32x4 rs = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD), live ? UNIT : 0);
+        const uint32_t dst = sub_lds + (uint32_t)((u % NU) * UNIT);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            R.r[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, s * 64, 0));
-        __builtin_amdgcn_sched_barrier(0);  // keep the whole page's loads ahead of the math
+        for (int i = 0; i < LPU; ++i)
+            ring_load16<true>(rs, dst + i * 1024, src_off(i));
     };
-    // Scores of page i (this wave's dims; with paired waves the two halves are added in a
-    // fixed order, low dims first), online-softmax update and rescale of the accumulator.
-    // Returns P^T (bf16, the B operand of the PV product) and the lane's valid tokens.
-    auto qk_softmax = [&](PageRegs &K, int i, bool (&valid)[4]) {
-        const int t0 = page_of(i) * kPage;
-        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+
+    // Q and the first page ids are in registers before the stream starts, so that the only
+    // vector-memory operations the waits below count are the stream's own loads.
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            st = mfma_k32(K.r[s], *(const u32x4 *)(q_lane + s * 32), st);
-        if (DS > 1) {
-            f32x4 *buf = sm_s[i & 1];
-            buf[wave * 64 + lane] = st;
-            __syncthreads();
-            const f32x4 other = buf[(wave ^ 1) * 64 + lane];
-            st = dpart == 0 ? st + other : other + st;
+    for (int u = 0; u < NU; ++u)
+        issue(u);
+
+    int u = 0;
+    for (int k = 0; k < my_pages; ++k) {
+        const int t0 = (pg0 + k * W + wave) * kPage;
+        // ---- K unit u landed once at most the NU - 1 later units' loads are outstanding
+        wait_vmcnt<(NU - 1) * LPU>();
+        const uint8_t *ks = sub + (u % NU) * UNIT;
+        f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKS; s += 2) {
+            st0 = mfma_k32(*(const u32x4 *)(ks + kbase[s & 3] + 256 * (s >> 2)), qb[s], st0);
+            st1 = mfma_k32(*(const u32x4 *)(ks + kbase[(s + 1) & 3] + 256 * ((s + 1) >> 2)), qb[s + 1], st1);
         }
-        // lane holds S^T[token t0 + 4*r4 + e][head c16]; out-of-range tokens are selected
-        // out (a NaN in an unused slot never reaches the sums)
+        f32x4 st = st0 + st1;
+        if (!SHARED)
+            issue(u + NU);
+
+        // ---- online softmax; lane holds S^T[token t0 + 4 r4 + e][head c16]. Tokens outside
+        // [tb, te) are selected out (a NaN in an unused slot never reaches the sums).
+        bool valid[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = t0 + 4 * r4 + e;
             valid[e] = t >= tb && t < te;
-            const float v = valid[e] ? st[e] * a.scale_log2 : -INFINITY;
-            st[e] = v;
-            mx = fmaxf(mx, v);
+            st[e] = valid[e] ? st[e] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, st[e]);
         }
-        mx = rows_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        // The reference maximum follows the running maximum exactly (rescaling whenever it
+        // grows), so the largest weight of a column is exactly 1.0 and carries no bf16 rounding
+        // into the PV product; sharply peaked rows stay accurate.
+        const float m_new = fmaxf(m_run, rows_max4(mx));
+        const bool resc = m_new > m_run;
+        const float alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
+        if (resc)
+            m_run = m_new;
         float ps[4], rs = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            ps[e] = fast_exp2(st[e] - m_new);
+            ps[e] = fast_exp2(st[e] - m_run);
             rs += ps[e];
         }
-        rs = rows_sum(rs);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        l_run = l_run * alpha + rows_sum4(rs);
+        if (__builtin_amdgcn_ballot_w64(resc)) {
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                acc[j] *= alpha;
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[dt] *= alpha;
         }
-        return u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
-    };
-    // O^T += V^T P^T for page i; V^T comes from an exact MFMA transpose of the V registers.
-    auto pv = [&](PageRegs &V, int i, u32x2 pb, const bool (&valid)[4]) {
-        const int t0 = page_of(i) * kPage;
-        const bool edge = t0 < tb || t0 + kPage > te;  // page holds tokens outside [tb, te)
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        __builtin_amdgcn_sched_barrier(0);
-        if (edge) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                f32x4 vt = mfma_k32(V.r[j >> 1], ident[j & 1], zero);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    vt[e] = valid[e] ? vt[e] : 0.f;
-                const u32x2 va = {pack_exact_bf16x2(vt[0], vt[1]), pack_exact_bf16x2(vt[2], vt[3])};
-                acc[j] = mfma_k16(va, pb, acc[j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const f32x4 vt = mfma_k32(V.r[j >> 1], ident[j & 1], zero);
-                const u32x2 va = {pack_exact_bf16x2(vt[0], vt[1]), pack_exact_bf16x2(vt[2], vt[3])};
-                acc[j] = mfma_k16(va, pb, acc[j]);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // One page of the group: its scores (always, so paired waves meet at their barrier),
-    // then the softmax update and PV product if the page exists for this group.
-    auto page_step = [&](PageRegs &K, PageRegs &V, int i) {
-        bool valid[4];
-        if (DS > 1 && i >= cnt) {  // dummy trip: only the partial-score exchange
-            f32x4 *buf = sm_s[i & 1];
-            buf[wave * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-            __syncthreads();
-            return;
-        }
-        const u32x2 pb = qk_softmax(K, i, valid);
-        pv(V, i, pb, valid);
-    };
+        const u32x2 pb = {pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
 
-    // ---- pipeline: K one page ahead of the math; V too when there is room (VBUF = 2),
-    // otherwise V's single buffer is refilled right after each PV product (VBUF = 1)
-    constexpr int VBUF = (SHARED || OCC == 1) ? 2 : 1;
-    PageRegs KA, KB, VA, VB;
-    load_regs(KA, page_rsrc(a.k_pool, 0, 0));  // unconditional: empty resource when cnt == 0
-    if (!SHARED)
-        load_regs(VA, page_rsrc(a.v_pool, 0, 0));
+        // ---- O^T += V^T P^T over the whole head dimension
+        const int uv = SHARED ? u : u + 1;
+        if (!SHARED)
+            wait_vmcnt<(NU - 1) * LPU>();
+        uint8_t *vs = sub + (uv % NU) * UNIT;
+        // Tokens outside [tb, te) carry P = 0, but their V slot may hold anything (a NaN, say,
+        // and 0 * NaN is NaN): on the split's first and last page their V rows are zeroed in
+        // the slice before the product. (With K = V the scores have already been read.)
+        if (t0 < tb || t0 + kPage > te) {
 #pragma unroll
-    for (int k = 0; k < kQItems; ++k) {
-        const int e = threadIdx.x + k * kThreads;
-        *(u32x4 *)(sm_q + (e / (HD / 8)) * kQStride + (e % (HD / 8)) * 8) = qv[k];
+            for (int r = 0; r < kPage; ++r) {
+                const int t = t0 + r;
+                if ((t < tb || t >= te) && lane * 16 < HD * 2)
+                    *(u32x4 *)(vs + r * HD * 2 + lane * 16) = u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            acc[dt] = mfma_k16(tr_read(vs + vbase[dt & 7] + 256 * (dt >> 3)), pb, acc[dt]);
+        issue(uv + NU);
+        u = uv + 1;
+    }
+    // No stream load (the zero-filling ones past the wave's pages included) may still be
+    // writing LDS when the slices are reused below.
+    wait_vmcnt<0>();
+
+    // ---- merge the four wave states (fixed order) and write this split's result
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad_page) != 0;
+    if (lane == 0)
+        sm_bad[wave] = wave_bad;
+    if (r4 == 0) {
+        sm_m[wave][c16] = m_run;
+        sm_l[wave][c16] = l_run;
+    }
+    __syncthreads();  // every wave is done with its slice; the states are visible
+    float *const mo = (float *)ring;  // [W][g][HD] fp32, each wave's acc scaled to the common max
+    {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            M = fmaxf(M, sm_m[w][c16]);
+        const float cw = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+        if (c16 < g) {
+            float *dst = mo + ((size_t)wave * g + c16) * HD + 4 * r4;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                *(f32x4 *)(dst + 16 * dt) = acc[dt] * cw;
+        }
     }
     __syncthreads();
-
-    for (int i = 0; i < trips; i += 2) {
-        // page ids: the block of 64 holding page i is `ids`, the following block `ids_next`
-        if ((i & 63) == 0 && i > 0) {
-            ids = ids_next;
-            ids_next = load_ids(i + 64);
+    bool bad = bad_len;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+        bad = bad || sm_bad[w];
+    for (int e = threadIdx.x * 4; e < g * HD; e += kThreads * 4) {
+        const int hn = e / HD, d = e % HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            M = fmaxf(M, sm_m[w][hn]);
+        float lsum = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float mw = sm_m[w][hn];
+            lsum += mw == -INFINITY ? 0.f : fast_exp2(mw - M) * sm_l[w][hn];
+            o += *(const f32x4 *)(mo + ((size_t)w * g + hn) * HD + d);
         }
-        const int ib = i & ~63;  // page index of ids' lane 0
-        // page i in KA/VA; page i+1 goes to KB (and VB, or VA after the PV product)
-        load_regs(KB, page_rsrc(a.k_pool, i + 1, ib));
-        if (!SHARED && VBUF == 2)
-            load_regs(VB, page_rsrc(a.v_pool, i + 1, ib));
-        page_step(KA, SHARED ? KA : VA, i);
-        if (!SHARED && VBUF == 1)
-            load_regs(VA, page_rsrc(a.v_pool, i + 1, ib));
-        if (i + 1 >= trips)
-            break;
-        // page i+1 in KB/(VB or VA); page i+2 goes to KA (and VA)
-        load_regs(KA, page_rsrc(a.k_pool, i + 2, ib));
-        if (!SHARED && VBUF == 2)
-            load_regs(VA, page_rsrc(a.v_pool, i + 2, ib));
-        page_step(KB, SHARED ? KB : (VBUF == 2 ? VB : VA), i + 1);
-        if (!SHARED && VBUF == 1)
-            load_regs(VA, page_rsrc(a.v_pool, i + 2, ib));
-    }
-
-    // ---- merge the page groups (fixed order) and write this split's result
-    if (dpart == 0 && r4 == 0) {
-        sm_m[grp][c16] = m_run;
-        sm_l[grp][c16] = l_run;
-    }
-    if (lane == 0)
-        sm_bad[wave] = bad_page;
-    for (int h0 = 0; h0 < g; h0 += kChunk) {
-        __syncthreads();
-        if (c16 >= h0 && c16 < min(g, h0 + kChunk)) {
-            float *dst = sm_o + (grp * kChunk + (c16 - h0)) * HD + dpart * kDimsPerWave + 4 * r4;
+        const float inv = 1.0f / lsum;
+        float lse = (M + fast_log2(lsum)) * kLn2;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
-                *(f32x4 *)(dst + 16 * j) = acc[j];
-        }
-        __syncthreads();
-        bool bad = bad_len;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            bad = bad || sm_bad[w];
-        const int nh = min(g, h0 + kChunk) - h0;
-        for (int e = threadIdx.x; e < nh * HD; e += kThreads) {
-            const int hn = h0 + e / HD, d = e % HD;
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NGRP; ++w)
-                M = fmaxf(M, sm_m[w][hn]);
-            float lsum = 0.f, o = 0.f;
-#pragma unroll
-            for (int w = 0; w < NGRP; ++w) {
-                const float mw = sm_m[w][hn];
-                if (mw == -INFINITY)
-                    continue;
-                const float wt = fast_exp2(mw - M);
-                lsum += wt * sm_l[w][hn];
-                o += wt * sm_o[(w * kChunk + (hn - h0)) * HD + d];
-            }
-            o = o / lsum;
-            float lse = (M + fast_log2(lsum)) * kLn2;
-            if (bad) {
-                o = __builtin_nanf("");
-                lse = __builtin_nanf("");
-            }
-            const int64_t bh = (int64_t)b * Hq + kvh * g + hn;
-            if (direct) {
-                a.out[bh * HD + d] = (uint16_t)bf16_rne(o);
-                if (d == 0)
-                    a.lse[bh] = lse;
-            } else {
-                a.o_part[(bh * a.n_slots + slot) * HD + d] = o;
-                if (d == 0)
-                    a.lse_part[bh * a.n_slots + slot] = lse;
-            }
+        for (int i = 0; i < 4; ++i)
+            o[i] = bad ? __builtin_nanf("") : o[i] * inv;
+        if (bad)
+            lse = __builtin_nanf("");
+        const int64_t bh = (int64_t)b * Hq + kvh * g + hn;
+        if (direct) {
+            *(u32x2 *)(a.out + bh * HD + d) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            if (d == 0)
+                a.lse[bh] = lse;
+        } else {
+            *(f32x4 *)(a.o_part + (bh * a.n_slots + slot) * HD + d) = o;
+            if (d == 0)
+                a.lse_part[bh * a.n_slots + slot] = lse;
         }
     }
 }
 
+// Launch shape per head_dim: waves per workgroup and LDS bytes per wave, measured on the
+// decode workloads of both families. head_dim 512 (16 KB units): one wave with two units per
+// workgroup, four workgroups per CU, so a batch's (row, KV head, split) items mostly start
+// at once and no CU waits on a partly filled last round. head_dim 256 (8 KB units): two
+// waves with three units each, three workgroups per CU, which keeps the window-sized local
+// items (at most 1024 keys) from running one page at a time on few waves.
+template <int HD>
+struct DecodeShape;
+template <>
+struct DecodeShape<512> {
+    static constexpr int waves = 1, slice = 32 * 1024;
+};
+template <>
+struct DecodeShape<256> {
+    static constexpr int waves = 2, slice = 24 * 1024;
+};
+
 template <int HD, bool SHARED>
 hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+    constexpr int W = DecodeShape<HD>::waves;
+    constexpr int SLICE = DecodeShape<HD>::slice;
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, kOcc>, grid, dim3(kThreads), args, 0,
+    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, SLICE>, grid, dim3(W * 64), args, 0,
                            stream);
 }
 

@@ -47,8 +47,6 @@ constexpr int kRingBytes = 128 * 1024;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -61,38 +59,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // hit 16 different 16-byte bank groups and (ii) the four tokens x two chunks of one
 // transpose-read lane group hit 8 different ones.
 __device__ __forceinline__ int swz(int x) { return ((x & 3) << 1) | ((x >> 2) & 1) | (x & 8); }
-
-// The ring's direct buffer->LDS loads and the waits on them are inline assembly: the
-// compiler sees neither, so it never orders its own LDS reads behind in-flight ring loads;
-// the ring is synchronised by exactly one "at most N loads outstanding" wait plus a barrier
-// per unit.
-//
-// 16 bytes per lane from the buffer `rsrc` at byte offset voffset into LDS at lds + 16 * lane
-// (M0 holds the LDS base; it is saved and restored around the load).
-__device__ __forceinline__ void ring_load16(u32x4 rsrc, uint32_t lds, uint32_t voffset) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voffset), "s"(rsrc), "s"(lds)
-        : "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Raw buffer resource: base address, no stride, `bytes` in range (0: every load returns
-// zeros and touches no memory).
-__device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
 
 // Four K-steps of the score product S^T += K . Q^T in VGPRs. The PV accumulators fill the
 // AGPR file, so the score tile must live in VGPRs; the compiler would place any MFMA result
@@ -143,10 +109,6 @@ __device__ __forceinline__ void scale_acc(f32x16 &c, float al) {
         c[v + 2] = x2;
         c[v + 3] = x3;
     }
-}
-
-__device__ __forceinline__ u32x2 tr_read(const uint8_t *p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
 }
 
 template <int HD, bool SHARED>
