@@ -40,6 +40,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// The bf16 values in the low / high half of a packed pair, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -38,6 +38,7 @@ namespace gattn {
 
 namespace {
 
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // LDS layout of one unit (one page's K or V for one KV head: 16 token rows of HD bf16):
 // token row t at t * HD * 2 bytes, its 16-byte chunk c at chunk slot c ^ dswz(t). dswz is a
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
     __shared__ float sm_m[W][16];
-    __shared__ float sm_l[W][16];
+    __shared__ float sm_l[W][16];   // row sums of the bf16 weights (normalise O)
+    __shared__ float sm_lx[W][16];  // row sums of the fp32 weights (LSE)
     __shared__ int sm_bad[W];
 
     const int lane = threadIdx.x & 63;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
         acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, l_ex = 0.f;
     int bad_page = 0;
     uint8_t *const sub = ring + wave * SUB;
     const uint32_t sub_lds = (uint32_t)(uintptr_t)sub;
@@ -249,27 +251,31 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
             st[e] = valid[e] ? st[e] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, st[e]);
         }
-        // The reference maximum follows the running maximum exactly (rescaling whenever it
-        // grows), so the largest weight of a column is exactly 1.0 and carries no bf16 rounding
-        // into the PV product; sharply peaked rows stay accurate.
+        // Lazy rescale: a column keeps its reference maximum until a score exceeds it by more
+        // than 2^8, so P stays below 256 and the accumulators are rescaled only on those pages.
+        // O is normalised by the sum of the bf16-rounded weights the PV product uses, so a
+        // weight's rounding scales numerator and denominator alike (a single dominant key gives
+        // exactly its V row, whatever the reference); the LSE uses the sum of the fp32 weights.
+        // Both share the reference maximum.
         const float m_new = fmaxf(m_run, rows_max4(mx));
-        const bool resc = m_new > m_run;
+        const bool resc = m_new > m_run + kRescaleLog2;
         const float alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
         if (resc)
             m_run = m_new;
-        float ps[4], rs = 0.f;
+        float ps[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4; ++e)
             ps[e] = fast_exp2(st[e] - m_run);
-            rs += ps[e];
-        }
+        const u32x2 pb = {pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
+        const float rs = ((bf16_lo(pb[0]) + bf16_hi(pb[0])) + bf16_lo(pb[1])) + bf16_hi(pb[1]);
+        const float rx = ((ps[0] + ps[1]) + ps[2]) + ps[3];
         l_run = l_run * alpha + rows_sum4(rs);
+        l_ex = l_ex * alpha + rows_sum4(rx);
         if (__builtin_amdgcn_ballot_w64(resc)) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 acc[dt] *= alpha;
         }
-        const u32x2 pb = {pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
 
         // ---- O^T += V^T P^T over the whole head dimension
         const int uv = SHARED ? u : u + 1;
@@ -297,13 +303,14 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     // writing LDS when the slices are reused below.
     wait_vmcnt<0>();
 
-    // ---- merge the four wave states (fixed order) and write this split's result
+    // ---- merge the wave states (fixed order) and write this split's result
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad_page) != 0;
     if (lane == 0)
         sm_bad[wave] = wave_bad;
     if (r4 == 0) {
         sm_m[wave][c16] = m_run;
         sm_l[wave][c16] = l_run;
+        sm_lx[wave][c16] = l_ex;
     }
     __syncthreads();  // every wave is done with its slice; the states are visible
     float *const mo = (float *)ring;  // [W][g][HD] fp32, each wave's acc scaled to the common max
@@ -331,16 +338,18 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int w = 0; w < W; ++w)
             M = fmaxf(M, sm_m[w][hn]);
-        float lsum = 0.f;
+        float lsum = 0.f, lxsum = 0.f;
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float mw = sm_m[w][hn];
-            lsum += mw == -INFINITY ? 0.f : fast_exp2(mw - M) * sm_l[w][hn];
+            const float cw = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            lsum += cw * sm_l[w][hn];
+            lxsum += cw * sm_lx[w][hn];
             o += *(const f32x4 *)(mo + ((size_t)w * g + hn) * HD + d);
         }
         const float inv = 1.0f / lsum;
-        float lse = (M + fast_log2(lsum)) * kLn2;
+        float lse = (M + fast_log2(lxsum)) * kLn2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[i] = bad ? __builtin_nanf("") : o[i] * inv;
