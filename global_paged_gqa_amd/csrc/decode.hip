@@ -40,44 +40,6 @@ namespace {
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-// LDS layout of one unit (one page's K or V for one KV head: 16 token rows of HD bf16):
-// token row t at t * HD * 2 bytes, its 16-byte chunk c at chunk slot c ^ dswz(t). dswz is a
-// bijection of the four token bits whose values for tokens 0..7 (and for 8..15) differ above
-// bit 0, so that (i) a K operand read (16 tokens at one chunk) hits 16 different 16-byte bank
-// groups and (ii) a transpose read of a 16-dim tile (8 tokens x 2 adjacent chunks in each half
-// wave) hits 16. Token rows are multiples of 256 bytes, so only the chunk slot picks the bank.
-__device__ __forceinline__ int dswz(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
-
-// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
-// gfx950 lane swaps. v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0
-// and 2 of its second; with both operands holding x, each lane ends up with its own value in
-// one register and its row partner's (lane l^16) in the other. v_permlane32_swap does the same
-// for lanes l and l^32. Written as assembly: given two copies of one value, the compiler folds
-// the builtins' two results into one. Both reductions are symmetric, so all four lanes of a
-// column get the identical value.
-__device__ __forceinline__ void swap_rows16(float &a, float &b) {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap_halves32(float &a, float &b) {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-
-__device__ __forceinline__ float rows_max4(float x) {
-    float a = x, b = x;
-    swap_rows16(a, b);
-    float c = fmaxf(a, b), d = c;
-    swap_halves32(c, d);
-    return fmaxf(c, d);
-}
-
-__device__ __forceinline__ float rows_sum4(float x) {
-    float a = x, b = x;
-    swap_rows16(a, b);
-    float c = a + b, d = c;
-    swap_halves32(c, d);
-    return c + d;
-}
-
 template <int HD, bool SHARED, int W, int kSliceBytes>
 __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     // W waves, each an independent page stream through its own kSliceBytes of LDS
