@@ -18,8 +18,13 @@
 // SIMD). head_dim 256: eight waves of 16 rows (16x16x32 MFMA; two waves per SIMD, so the
 // hardware overlaps one wave's softmax and waits with the other's matrix work).
 // K and V blocks stream through a 128 KB LDS ring filled by direct global->LDS buffer
-// loads in the order of their first use, one barrier per block. Iteration j computes the
-// scores of block j+1 and then the PV product of block j beside the softmax of block j+1.
+// loads in the order of their first use. Iteration j computes the scores of block j+1 and
+// then the PV product of block j beside the softmax of block j+1. With separate K and V pools
+// (head_dim 512) it has two barriers: the one before the scores frees the slot of the V just
+// used and the one before the PV product frees the slot of the K just used, so each K unit is
+// requested two blocks ahead of its scores. The ring loads are spread between the MFMA groups
+// of both products rather than issued in one burst, because a wave stalls on the issue of a
+// global->LDS load while the load unit is busy.
 //
 // The online softmax rescales lazily: a row keeps its reference maximum until a new score
 // exceeds it by more than 2^8, so P stays below 256 and the accumulators are rescaled only
@@ -120,9 +125,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     constexpr int NU = kRingBytes / UNIT;            // ring depth in units
     constexpr int LPU = UNIT / 16 / kThreads;        // 16-byte loads per lane per unit
     constexpr int PAGE_BYTES = kPage * HD * 2;       // one (page, KV head) block
-    // units that may still be in flight when an iteration starts (the ones it reads have landed)
-    constexpr int AHEAD = SHARED ? NU - 3 : NU - 4;
-    static_assert(AHEAD >= 0 && LPU % 2 == 0 && (NU - 1) * LPU + 1 <= 63, "ring shape");
+    // K = V: units that may still be in flight when an iteration starts (the ones it reads have
+    // landed). Separate pools keep four units in the ring (two read, two in flight).
+    constexpr int AHEAD = NU - 3;
+    static_assert(NU >= 4 && LPU % 2 == 0 && (NU - 1) * LPU + 1 <= 63, "ring shape");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
 
@@ -291,8 +297,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const float scale = a.scale_log2;
     // S^T[32 tok][32 rows] of block j for this wave's rows. Operand reads run one group of four
     // K-steps ahead of the MFMAs; the scheduling fences keep the compiler from hoisting every
-    // read of the block (which would not fit beside Q in registers).
-    auto qk = [&](int j, f32x16 &st) {
+    // read of the block (which would not fit beside Q in registers). hook(t) runs after group t
+    // (ring loads issued between the MFMA groups).
+    auto qk = [&](int j, f32x16 &st, auto hook) {
         const uint8_t *kst = ring + (unit_k(j) % NU) * UNIT;
         auto kread = [&](int s) { return *(const u32x4 *)(kst + kb[s & 7] + 256 * (s >> 3)); };
         u32x4 kf[2][4];
@@ -311,6 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 qk4<true>(st, kk[0], kk[1], kk[2], kk[3], qb[0], qb[1], qb[2], qb[3]);
             else
                 qk4<false>(st, kk[0], kk[1], kk[2], kk[3], qb[4 * t], qb[4 * t + 1], qb[4 * t + 2], qb[4 * t + 3]);
+            hook(t);
             __builtin_amdgcn_sched_barrier(0);
         }
         qk_settle(st);
@@ -360,31 +368,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         l_ex = l_ex * alpha + halves_sum(rx);
     };
     // O^T += V^T P^T for block j over the whole head dimension, V^T fragments read one tile
-    // ahead of the MFMAs. Tokens no row of the tile can see (before the window, past the last
-    // query) carry P = 0; on the blocks that hold such tokens their V (possibly a never-written
-    // slot) is selected out rather than multiplied by zero.
-    auto pv = [&](int j, const u32x4 pf0, const u32x4 pf1) {
+    // ahead of the MFMAs. Tokens no row of the tile can see carry P = 0, and their V rows are
+    // zeroed in LDS beforehand (clear_edge), so a never-written slot cannot turn 0 * V into a
+    // NaN. hook(dt) runs after tile dt.
+    auto pv = [&](int j, const u32x4 pf0, const u32x4 pf1, auto hook) {
         const uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
-        const int T0 = kb0 + j * kTok;
-        // keep masks (all ones on blocks inside [lo, p_last]); applied unconditionally so the
-        // loop below stays one basic block the scheduler can interleave with the softmax
-        u32x4 keep0, keep1;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int w2 = 0; w2 < 2; ++w2) {
-                uint32_t k0 = 0, k1 = 0;
-#pragma unroll
-                for (int r2 = 0; r2 < 2; ++r2) {
-                    const int r = 2 * w2 + r2;
-                    const uint32_t m = r2 ? 0xFFFF0000u : 0x0000FFFFu;
-                    const int Ta = T0 + 8 * i + 4 * h + r, Tb = Ta + 16;
-                    k0 |= (Ta >= lo && Ta <= p_last) ? m : 0u;
-                    k1 |= (Tb >= lo && Tb <= p_last) ? m : 0u;
-                }
-                keep0[2 * i + w2] = k0;
-                keep1[2 * i + w2] = k1;
-            }
         auto vread = [&](int dt, int p) {
             const uint32_t o = 256 * (dt >> 2) + p * PAGE_BYTES;
             const u32x2 v0 = tr_read(vst + vb[0][dt & 3] + o);
@@ -399,46 +387,85 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 na0 = vread(dt + 1, 0);
                 na1 = vread(dt + 1, 1);
             }
-            acc[dt] = mfma32(va0 & keep0, pf0, acc[dt]);
-            acc[dt] = mfma32(va1 & keep1, pf1, acc[dt]);
+            acc[dt] = mfma32(va0, pf0, acc[dt]);
+            acc[dt] = mfma32(va1, pf1, acc[dt]);
+            hook(dt);
             if (dt + 1 < NDT) {
                 va0 = na0;
                 va1 = na1;
             }
         }
     };
+    // Zero the V rows of block j that no row of the tile can see (tokens before lo or past
+    // p_last: only the first and last blocks have them). Called with block j's V landed for
+    // every wave; returns whether it wrote, in which case the caller synchronises again.
+    auto clear_edge = [&](int j) {
+        const int T0 = kb0 + j * kTok;
+        if (T0 >= lo && T0 + kTok - 1 <= p_last)
+            return false;
+        uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
+        for (int t = wave; t < kTok; t += kWaves) {
+            const int T = T0 + t;
+            if (T < lo || T > p_last)
+                for (int c = lane; c < HD / 8; c += 64)
+                    *(u32x4 *)(vst + t * HD * 2 + c * 16) = u32x4{0, 0, 0, 0};
+        }
+        return true;
+    };
+    // Ring loads of one unit spread over the N MFMA groups of a product: group i issues loads
+    // [i*LPU/N, (i+1)*LPU/N) of the unit.
+    auto spread = [&](const UnitLoad &ul, auto n_groups) {
+        constexpr int N = decltype(n_groups)::value;
+        return [&ul, &emit](int i) {
+#pragma unroll
+            for (int k = i * LPU / N; k < (i + 1) * LPU / N; ++k)
+                emit(ul, k);
+        };
+    };
+    auto no_hook = [](int) {};
 
     // Q and the first page ids are in registers before the ring starts, so that inside the
     // block loop the only vector-memory operations in flight are the ring's own loads.
     __builtin_amdgcn_s_waitcnt(0);
+    // Separate pools: units 0..3 (K0, K1, V0, K2) before the loop; iteration j then issues the V
+    // of block j+1 (unit 2j+4) after its first barrier and the K of block j+3 (unit 2j+5) after
+    // the second, so a K unit is loaded two blocks ahead of its scores and a V unit one block
+    // and a half ahead of its product. K = V: units 0 .. NU-2, then unit j+NU-1 per iteration.
+    constexpr int PRO = SHARED ? NU - 1 : 4;
 #pragma unroll
-    for (int u = 0; u < NU - 1; ++u)
+    for (int u = 0; u < PRO; ++u)
         issue(u);
-    wait_vmcnt<(NU - 2) * LPU>();  // unit 0 (the K of block 0) landed for this wave
+    wait_vmcnt<(PRO - 1) * LPU>();  // unit 0 (the K of block 0) landed for this wave
     __syncthreads();
     f32x16 st;
     u32x4 pf[2];
     float alpha;
-    qk(0, st);
+    qk(0, st, no_hook);
     softmax(0, st, pf, alpha);
 
     // Iteration j: the scores of block j+1 (QK), then the PV product of block j interleaved by
     // the scheduler with the softmax of block j+1 (independent MFMA and VALU work).
     for (int j = 0; j < nblk; ++j) {
-        // this iteration's units (block j+1's K, block j's V) landed for this wave; after the
-        // barrier for all waves, and the slots of the previous iteration's units are free
-        wait_vmcnt<AHEAD * LPU>();
-        __syncthreads();
-        if (SHARED) {
-            issue(j + NU - 1);
-        } else {
-            issue(2 * j + NU - 1);
-            issue(2 * j + NU);
-        }
-        // The next block's scores are computed even in the last iteration: block nblk lies
-        // past every query (fully masked, its units zero-filled), so it changes no state.
         f32x16 st1;
-        qk(j + 1, st1);
+        if (SHARED) {
+            // unit j+1 landed for this wave; after the barrier for all waves, and unit j-1's slot
+            // (read by the previous PV) is free
+            wait_vmcnt<AHEAD * LPU>();
+            __syncthreads();
+            if (clear_edge(j))
+                __syncthreads();
+            const UnitLoad ul = prep(j + NU - 1);
+            qk(j + 1, st1, spread(ul, std::integral_constant<int, NKS / 4>{}));
+        } else {
+            // the K of block j+1 landed (units 2j+2 and 2j+3 may be in flight); after the barrier
+            // for all waves, and the slot of block j-1's V is free
+            wait_vmcnt<2 * LPU>();
+            __syncthreads();
+            const UnitLoad ul = prep(2 * j + 4);
+            // The next block's scores are computed even in the last iteration: block nblk lies
+            // past every query (fully masked, its units zero-filled), so it changes no state.
+            qk(j + 1, st1, spread(ul, std::integral_constant<int, NKS / 4>{}));
+        }
         // rescale this wave's rows for block j (factors from its softmax)
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -447,7 +474,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
         u32x4 pf1[2];
         float alpha1;
-        pv(j, pf[0], pf[1]);
+        if (SHARED) {
+            pv(j, pf[0], pf[1], no_hook);
+        } else {
+            // the V of block j landed (units 2j+3 and 2j+4 may be in flight); after the barrier
+            // for all waves, and the slot of block j+1's K (read by the QK above) is free
+            wait_vmcnt<2 * LPU>();
+            __syncthreads();
+            if (clear_edge(j))
+                __syncthreads();
+            const UnitLoad ul = prep(2 * j + 5);
+            pv(j, pf[0], pf[1], spread(ul, std::integral_constant<int, NDT>{}));
+        }
         softmax(j + 1, st1, pf1, alpha1);
         pf[0] = pf1[0];
         pf[1] = pf1[1];
@@ -774,9 +812,10 @@ __global__ __launch_bounds__(512, 1) void prefill16_kernel(PrefillArgs a) {
 template <int HD, bool SHARED>
 hipError_t launch(const PrefillArgs &a, dim3 grid, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    if (HD == 256)
+    if constexpr (HD == 256)
         return hipLaunchKernel((const void *)prefill16_kernel<HD, SHARED>, grid, dim3(512), args, 0, stream);
-    return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0, stream);
+    else
+        return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
