@@ -6,8 +6,8 @@
 // the flash-decode split factor of the Core AI card's "--metal-sdpa" section).
 // Local rows only visit the splits that intersect their window, so a row with a
 // 32768-token context still reads at most `window` keys (the sliding-window
-// tile pruning that page 5's "Three load-bearing facts" #1 credits with a 3-4x
-// gain).
+// tile pruning that the vllm-gemma-4-31b skills page, "Three load-bearing facts",
+// credits with a 3-4x gain).
 //
 // Memory path. Decode reads every visible K/V byte exactly once, so it is bound by
 // HBM bandwidth. Each page's (page, KV head) block is contiguous in the pool, and it

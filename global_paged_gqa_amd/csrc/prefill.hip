@@ -14,17 +14,18 @@
 //   PV: O^T[dims][rows] += V^T . P^T over the whole head_dim, with V^T read from the
 //       row-major page by the gfx950 transpose read (ds_read_b64_tr_b16) and P^T taken
 //       straight from the score tile's accumulator layout.
-// head_dim 512: four waves of 32 rows (32x32x16 MFMA, accumulators in AGPRs; one wave per
-// SIMD). head_dim 256: eight waves of 16 rows (16x16x32 MFMA; two waves per SIMD, so the
-// hardware overlaps one wave's softmax and waits with the other's matrix work).
+// Four waves of 32 rows each (32x32x16 MFMA), the O accumulators in AGPRs: 256 of them at
+// head_dim 512, 128 at head_dim 256; one wave per SIMD either way (rows per wave set the LDS
+// traffic: every wave reads the whole K and V block, so fewer, fatter waves read less).
 // K and V blocks stream through a 128 KB LDS ring filled by direct global->LDS buffer
 // loads in the order of their first use. Iteration j computes the scores of block j+1 and
-// then the PV product of block j beside the softmax of block j+1. With separate K and V pools
-// (head_dim 512) it has two barriers: the one before the scores frees the slot of the V just
-// used and the one before the PV product frees the slot of the K just used, so each K unit is
-// requested two blocks ahead of its scores. The ring loads are spread between the MFMA groups
-// of both products rather than issued in one burst, because a wave stalls on the issue of a
-// global->LDS load while the load unit is busy.
+// then the PV product of block j with the softmax of block j+1 placed step by step between
+// its MFMAs (VALU work beside the matrix core). With separate K and V pools it has two
+// barriers: the one before the scores frees the slot of the V just used and the one before
+// the PV product frees the slot of the K just used, so each K unit is requested two blocks
+// ahead of its scores. The ring loads are spread between the MFMA groups of both products
+// rather than issued in one burst, because a wave stalls on the issue of a global->LDS load
+// while the load unit is busy. Each wave prepares the buffer resource of one page per unit.
 //
 // The online softmax rescales lazily: a row keeps its reference maximum until a new score
 // exceeds it by more than 2^8, so P stays below 256 and the accumulators are rescaled only
@@ -33,7 +34,8 @@
 // result is the exact softmax up to rounding.
 //
 // The key range of a tile is pruned to [first visible key of its first query, its last
-// query] (page 5's "Three load-bearing facts" #1: sliding-window tile pruning); pages in a
+// query] (the sliding-window tile pruning of the vllm-gemma-4-31b skills page, "Three
+// load-bearing facts", first item); pages in a
 // block that lie outside it are never read (zero-size buffer resource: zeros, no traffic).
 // Workgroups are mapped so that each XCD works through the query tiles of the same (row,
 // KV head), heaviest first, sharing that XCD's L2.
@@ -117,6 +119,63 @@ __device__ __forceinline__ void scale_acc(f32x16 &c, float al) {
     }
 }
 
+// Page resources of one tile's K/V stream. A ring unit is the K (or V) of one 32-token block,
+// two pages; waves [0, W/2) load its first page and waves [W/2, W) its second, so each wave
+// prepares one buffer resource per unit. The tile reads pages [pgA, pgA + npg); page rel
+// (relative to pgA) is read only if it holds a token in [lo, p_last], i.e. rel in [0, npg)
+// past the first r_lo pages, and its id is below num_pages. Any other page gets a zero-size
+// resource (its loads return zeros with no memory traffic), and an id out of range inside the
+// tile's range flags the tile. Page ids sit 64 per vector register (lane i: page base + i) and
+// are read back with readlane; the window slides every 32 blocks.
+template <int HD, int W>
+struct TilePages {
+    static constexpr int PAGE_BYTES = kPage * HD * 2;
+    static constexpr int WPP = W / 2;  // waves per page
+    const int32_t *pt;                 // the row's page table, from page pgA
+    int npg, r_lo;
+    uint32_t npages32;
+    uint64_t kbase, vbase, page_stride;
+    int ids, ids_next, ids_base;
+    int bad;
+
+    __device__ int load_ids(int first, int lane) const { return npg > 0 ? pt[min(first + lane, npg - 1)] : 0; }
+    __device__ void init(const PrefillArgs &a, int b, int kvh, int pgA, int npg_, int r_lo_, int lane) {
+        pt = a.page_table + (int64_t)b * a.pt_stride + pgA;
+        npg = npg_;
+        r_lo = r_lo_;
+        npages32 = (uint32_t)min<int64_t>(a.num_pages, INT32_MAX);
+        kbase = (uint64_t)(uintptr_t)(a.k_pool + (int64_t)kvh * kPage * HD);
+        vbase = (uint64_t)(uintptr_t)(a.v_pool + (int64_t)kvh * kPage * HD);
+        page_stride = (uint64_t)a.num_kv_heads * PAGE_BYTES;  // bytes between pages
+        ids = load_ids(0, lane);
+        ids_next = load_ids(64, lane);
+        ids_base = 0;
+        bad = 0;
+    }
+    // buffer resource of this wave's page of block blk in the K or V pool
+    __device__ u32x4 rsrc(int blk, bool is_v, int wave, int lane) {
+        const int rel = 2 * blk + wave / WPP;
+        if (rel < npg && rel - ids_base >= 96) {
+            ids = ids_next;
+            ids_base += 64;
+            ids_next = load_ids(ids_base + 64, lane);
+            // Wait for the ids here, on this rare path. Left to the compiler, the wait lands
+            // after the branch, on every call, and drains the ring loads in flight each time.
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        const bool in_range = rel >= r_lo && rel < npg;
+        const int r = (rel - ids_base) & 127;  // 0..127 for pages in range
+        const int id_a = __builtin_amdgcn_readlane(ids, r & 63);
+        const int id_b = __builtin_amdgcn_readlane(ids_next, r & 63);
+        const uint32_t pid = (uint32_t)(r >= 64 ? id_b : id_a);
+        const bool live = in_range && pid < npages32;
+        bad |= (int)(in_range && pid >= npages32);
+        const uint64_t addr = (is_v ? vbase : kbase) + (uint64_t)(live ? pid : 0u) * page_stride;
+        return u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xFFFFu, live ? (uint32_t)PAGE_BYTES : 0u,
+                     0x00020000u};
+    }
+};
+
 template <int HD, bool SHARED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     constexpr int NKS = HD / 16;                     // K-steps of the score product
@@ -131,6 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     static_assert(NU >= 4 && LPU % 2 == 0 && (NU - 1) * LPU + 1 <= 63, "ring shape");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
+    __shared__ int sm_bad;  // some wave met a page id out of range
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,6 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int kvh = (item / gridDim.x) % gridDim.y;
     const int b = item / (gridDim.x * gridDim.y);
 
+    if (threadIdx.x == 0)
+        sm_bad = 0;
     const int q0 = a.cu_q[b], q_len = a.cu_q[b + 1] - q0;
     const int L = a.ctx_lens[b];
     const int BQ = kRows / g;          // query positions per tile
@@ -165,7 +227,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int nblk = bad_row ? 0 : (p_last - kb0) / kTok + 1;
     const int pgA = kb0 / kPage;                                         // first page of block 0
     const int npg = bad_row ? 0 : p_last / kPage - pgA + 1;
-    const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
 
     // ---- this wave's rows: row m = 32 * wave + n32 is (query position m / g, head m % g)
     const int m_own = 32 * wave + n32;
@@ -193,71 +254,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         for (int v = 0; v < 16; ++v)
             acc[d][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f, l_ex = 0.f;
-    int bad_page = 0;
 
-    // ---- ring fill: load k of a unit writes LDS chunk position P = k*256 + wave*64 + lane,
-    // i.e. token row P / (HD/8), slot P % (HD/8); it fetches the chunk the swizzle puts there.
-    // Loads 0 .. LPU/2-1 cover the block's first page, the rest its second.
+    // ---- ring fill. Wave w loads page w / 2 of each unit: its load k writes the unit's LDS
+    // chunk position P = 1024 (w / 2) + 128 k + 64 (w % 2) + lane, i.e. token row P / (HD/8) of
+    // the block, slot P % (HD/8), and fetches the chunk the swizzle puts there.
+    using Pages = TilePages<HD, kWaves>;
+    static_assert(Pages::PAGE_BYTES / 16 == Pages::WPP * 64 * LPU, "one page per wave group");
+    Pages pages;
+    pages.init(a, b, kvh, pgA, npg, lo / kPage - pgA, lane);
+    auto chunk0 = [&](int k) { return (wave / Pages::WPP) * (Pages::PAGE_BYTES / 16) + k * Pages::WPP * 64 +
+                                      (wave % Pages::WPP) * 64; };
     auto src_off = [&](int k) {
-        const int P = k * kThreads + wave * 64 + lane;
+        const int P = chunk0(k) + lane;
         const int t = P / (HD / 8);
         const int c = (P % (HD / 8)) ^ swz(t & 15);
         return (uint32_t)((t & 15) * HD + c * 8) * 2u;
     };
-    // Page ids of the tile's range, 64 per vector register (lane j: page 64*k + j), read back
-    // with readlane so that the block loop never waits on a memory load for an id.
-    auto load_ids = [&](int first) {
-        return bad_row ? 0 : pt[pgA + min(first + lane, max(npg - 1, 0))];
-    };
-    int ids = load_ids(0), ids_next = load_ids(64);
-    int ids_base = 0;  // page index (relative to pgA) of ids' lane 0
     // The ring streams units in the order of their first use. Separate pools: unit 0 is the K
     // of block 0, unit 2j+1 the K of block j+1, unit 2j+2 the V of block j (iteration j reads
     // both). K = V: unit j is block j. Units past the last block, and pages of a block outside
     // [lo, p_last], load zeros with no memory traffic, so that every wave always has exactly
     // LPU loads per unit in flight and the ring waits stay exact.
     struct UnitLoad {
-        u32x4 rs[2];   // buffer resources of the block's two pages (zero size: not read)
-        uint32_t dst;  // this wave's LDS base for the unit
+        u32x4 rs;      // buffer resource of this wave's page (zero size: not read)
+        uint32_t dst;  // LDS address of the unit
     };
-    // Per page: the page id (two readlanes, no vector select), an unsigned range check, and the
-    // page's byte address, all in scalar registers without branches.
-    const uint32_t npages32 = (uint32_t)min<int64_t>(a.num_pages, INT32_MAX);
-    const uint64_t kbase = (uint64_t)(uintptr_t)(a.k_pool + (int64_t)kvh * kPage * HD);
-    const uint64_t vbase = (uint64_t)(uintptr_t)(a.v_pool + (int64_t)kvh * kPage * HD);
-    const uint64_t page_stride = (uint64_t)a.num_kv_heads * PAGE_BYTES;  // bytes between pages
     auto prep = [&](int u) {
         const int blk = SHARED ? u : (u == 0 ? 0 : ((u & 1) ? (u + 1) >> 1 : (u >> 1) - 1));
         const bool is_v = !SHARED && u > 0 && (u & 1) == 0;
-        if (blk < nblk && 2 * blk + 1 - ids_base >= 96) {  // slide the id window (every 32 blocks)
-            ids = ids_next;
-            ids_base += 64;
-            ids_next = load_ids(ids_base + 64);
-        }
-        const uint64_t base = is_v ? vbase : kbase;
-        UnitLoad ul;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const int rel = 2 * blk + pp;
-            const int pg = pgA + rel;
-            const bool in_range = blk < nblk && pg * kPage <= p_last && pg * kPage + kPage - 1 >= lo;
-            const int r = (rel - ids_base) & 127;  // 0..127 for pages in range
-            const int id_a = __builtin_amdgcn_readlane(ids, r & 63);
-            const int id_b = __builtin_amdgcn_readlane(ids_next, r & 63);
-            const uint32_t pid = (uint32_t)(r >= 64 ? id_b : id_a);
-            const bool valid = pid < npages32;
-            const bool live = in_range && valid;
-            bad_page |= (int)(in_range && !valid);
-            const uint64_t addr = base + (uint64_t)(live ? pid : 0u) * page_stride;
-            ul.rs[pp] = u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xFFFFu, live ? (uint32_t)PAGE_BYTES : 0u,
-                              0x00020000u};
-        }
-        ul.dst = (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT) + (uint32_t)(wave * 64 * 16);
-        return ul;
+        return UnitLoad{pages.rsrc(blk, is_v, wave, lane), (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT)};
     };
-    auto emit = [&](const UnitLoad &ul, int k) {
-        ring_load16(ul.rs[k < LPU / 2 ? 0 : 1], ul.dst + k * kThreads * 16, src_off(k));
-    };
+    auto emit = [&](const UnitLoad &ul, int k) { ring_load16(ul.rs, ul.dst + chunk0(k) * 16, src_off(k)); };
     auto issue = [&](int u) {
         const UnitLoad ul = prep(u);
 #pragma unroll
@@ -330,42 +357,65 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // O is normalised by the sum of the bf16-rounded weights the PV product uses (a weight's
     // rounding scales numerator and denominator alike), the LSE by the sum of the fp32 weights.
     // Returns the P^T fragments of the two 16-token K-steps; alpha is the rows' rescale factor.
-    auto softmax = [&](int j, f32x16 &st, u32x4 (&pf)[2], float &alpha) {
+    // The softmax runs in twelve steps so that the PV loop can place them between its MFMAs
+    // (VALU work beside the matrix core): 0-3 mask, scale and row maximum (four scores each),
+    // 4 the new reference maximum, 5-8 the exponentials, 9-10 the bf16 packing and the sums,
+    // 11 the row sums' update.
+    struct SmState {
+        int lim_lo, lim_hi;
+        float mx, mb, rs, rx;
+        float ps[16];
+    };
+    auto sm_init = [&](int j, SmState &z) {
         // visible iff T <= p_own (causal) and p_own - T < window (local): with the lane's token
         // offsets o(v) = 8(v/4) + 4h + v%4 from T0, that is lim_lo <= o(v) <= lim_hi
         const int T0 = kb0 + j * kTok;
-        const int lim_hi = p_own - T0;
-        const int lim_lo = a.is_global ? INT32_MIN : p_own - a.window + 1 - T0;
-        float mx = -INFINITY;
+        z.lim_hi = p_own - T0;
+        z.lim_lo = a.is_global ? INT32_MIN : p_own - a.window + 1 - T0;
+        z.mx = -INFINITY;
+        z.rs = 0.f;
+        z.rx = 0.f;
+    };
+    auto sm_step = [&](int step, SmState &z, f32x16 &st, u32x4 (&pf)[2], float &alpha) {
+        if (step < 4) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int o = 8 * (v >> 2) + 4 * h + (v & 3);
-            st[v] = (o <= lim_hi && o >= lim_lo) ? st[v] * scale : -INFINITY;
-            mx = fmaxf(mx, st[v]);
-        }
-        const float m_new = fmaxf(m_run, halves_max(mx));
-        const bool resc = m_new > m_run + kRescaleLog2;
-        alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
-        if (resc)
-            m_run = m_new;
-        const float mb = m_run == -INFINITY ? 0.f : m_run;
-        float ps[16];
+            for (int v = 4 * step; v < 4 * step + 4; ++v) {
+                const int o = 8 * (v >> 2) + 4 * h + (v & 3);
+                st[v] = (o <= z.lim_hi && o >= z.lim_lo) ? st[v] * scale : -INFINITY;
+                z.mx = fmaxf(z.mx, st[v]);
+            }
+        } else if (step == 4) {
+            const float m_new = fmaxf(m_run, halves_max(z.mx));
+            const bool resc = m_new > m_run + kRescaleLog2;
+            alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
+            if (resc)
+                m_run = m_new;
+            z.mb = m_run == -INFINITY ? 0.f : m_run;
+        } else if (step < 9) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            ps[v] = fast_exp2(st[v] - mb);
-        float rs = 0.f, rx = 0.f;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            pf[p] = u32x4{pack_bf16x2(ps[8 * p + 0], ps[8 * p + 1]), pack_bf16x2(ps[8 * p + 2], ps[8 * p + 3]),
-                          pack_bf16x2(ps[8 * p + 4], ps[8 * p + 5]), pack_bf16x2(ps[8 * p + 6], ps[8 * p + 7])};
+            for (int v = 4 * (step - 5); v < 4 * (step - 5) + 4; ++v)
+                z.ps[v] = fast_exp2(st[v] - z.mb);
+        } else if (step < 11) {
+            const int q = step - 9;
+            pf[q] = u32x4{pack_bf16x2(z.ps[8 * q + 0], z.ps[8 * q + 1]), pack_bf16x2(z.ps[8 * q + 2], z.ps[8 * q + 3]),
+                          pack_bf16x2(z.ps[8 * q + 4], z.ps[8 * q + 5]), pack_bf16x2(z.ps[8 * q + 6], z.ps[8 * q + 7])};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                rs += bf16_lo(pf[p][i]) + bf16_hi(pf[p][i]);
-                rx += ps[8 * p + 2 * i] + ps[8 * p + 2 * i + 1];
+                z.rs += bf16_lo(pf[q][i]) + bf16_hi(pf[q][i]);
+                z.rx += z.ps[8 * q + 2 * i] + z.ps[8 * q + 2 * i + 1];
             }
+        } else if (step == 11) {
+            l_run = l_run * alpha + halves_sum(z.rs);
+            l_ex = l_ex * alpha + halves_sum(z.rx);
         }
-        l_run = l_run * alpha + halves_sum(rs);
-        l_ex = l_ex * alpha + halves_sum(rx);
+    };
+    constexpr int SM_STEPS = 12;
+    auto softmax = [&](int j, f32x16 &st, u32x4 (&pf)[2], float &alpha) {
+        SmState z;
+        sm_init(j, z);
+#pragma unroll
+        for (int step = 0; step < SM_STEPS; ++step)
+            sm_step(step, z, st, pf, alpha);
     };
     // O^T += V^T P^T for block j over the whole head dimension, V^T fragments read one tile
     // ahead of the MFMAs. Tokens no row of the tile can see carry P = 0, and their V rows are
@@ -379,21 +429,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             const u32x2 v1 = tr_read(vst + vb[1][dt & 3] + o);
             return u32x4{v0[0], v0[1], v1[0], v1[1]};
         };
-        u32x4 va0 = vread(0, 0), va1 = vread(0, 1);
+        // fragments of tile dt in slot dt % PVA, read PVA - 1 tiles ahead of their MFMAs (the K
+        // fragments of the score product are dead here, so the registers are free)
+        constexpr int PVA = 3;
+        u32x4 vf[PVA][2];
+#pragma unroll
+        for (int d = 0; d < PVA - 1; ++d) {
+            vf[d][0] = vread(d, 0);
+            vf[d][1] = vread(d, 1);
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            u32x4 na0, na1;
-            if (dt + 1 < NDT) {
-                na0 = vread(dt + 1, 0);
-                na1 = vread(dt + 1, 1);
+            if (dt + PVA - 1 < NDT) {
+                vf[(dt + PVA - 1) % PVA][0] = vread(dt + PVA - 1, 0);
+                vf[(dt + PVA - 1) % PVA][1] = vread(dt + PVA - 1, 1);
             }
-            acc[dt] = mfma32(va0, pf0, acc[dt]);
-            acc[dt] = mfma32(va1, pf1, acc[dt]);
+            acc[dt] = mfma32(vf[dt % PVA][0], pf0, acc[dt]);
+            acc[dt] = mfma32(vf[dt % PVA][1], pf1, acc[dt]);
             hook(dt);
-            if (dt + 1 < NDT) {
-                va0 = na0;
-                va1 = na1;
-            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // Zero the V rows of block j that no row of the tile can see (tokens before lo or past
@@ -474,8 +528,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
         u32x4 pf1[2];
         float alpha1;
+        SmState z;
+        sm_init(j + 1, z);
+        // PV tile dt is followed by softmax steps [dt S / NDT, (dt + 1) S / NDT) of the next block
+        auto sm_hook = [&](int dt) {
+#pragma unroll
+            for (int step = dt * SM_STEPS / NDT; step < (dt + 1) * SM_STEPS / NDT; ++step)
+                sm_step(step, z, st1, pf1, alpha1);
+        };
         if (SHARED) {
-            pv(j, pf[0], pf[1], no_hook);
+            pv(j, pf[0], pf[1], sm_hook);
         } else {
             // the V of block j landed (units 2j+3 and 2j+4 may be in flight); after the barrier
             // for all waves, and the slot of block j+1's K (read by the QK above) is free
@@ -484,9 +546,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (clear_edge(j))
                 __syncthreads();
             const UnitLoad ul = prep(2 * j + 5);
-            pv(j, pf[0], pf[1], spread(ul, std::integral_constant<int, NDT>{}));
+            auto loads = spread(ul, std::integral_constant<int, NDT>{});
+            pv(j, pf[0], pf[1], [&](int dt) {
+                loads(dt);
+                sm_hook(dt);
+            });
         }
-        softmax(j + 1, st1, pf1, alpha1);
         pf[0] = pf1[0];
         pf[1] = pf1[1];
         alpha = alpha1;
@@ -495,9 +560,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // No ring load (the zero-filling ones past the last block included) may still be writing
     // this workgroup's LDS when it ends.
     wait_vmcnt<0>();
+    // the tile's verdict on its page ids, from every wave's pages
+    auto bad_tile = [&](int mine) {
+        if (mine)
+            sm_bad = 1;
+        __syncthreads();
+        return sm_bad != 0;
+    };
 
     // ---- this wave's rows: normalise and write O, LSE
-    const bool bad = bad_row || __builtin_amdgcn_ballot_w64(bad_page) != 0;
+    const bool bad = bad_row || bad_tile(pages.bad);
     if (!ok_own)
         return;
     const int64_t orow = (int64_t)(q0 + tile_q + pos_own) * Hq + kvh * g + m_own % g;
@@ -517,305 +589,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
 }
 
-// Eight-wave variant: the same 128 MFMA rows per workgroup, 16 rows per wave, with the
-// 16x16x32 MFMA for both products, so that two waves share each SIMD and the hardware overlaps
-// one wave's softmax, loads and waits with the other's matrix work. Per wave and 32-key block:
-//   QK: S^T[32 tok][16 rows] as two 16-key tiles (A = K rows from LDS, B = Q^T in registers);
-//   softmax of the rows (the row's 32 scores sit in four 16-lane groups: lane swaps);
-//   PV: O^T[16 dims][16 rows] += V^T[16 dims][32 tok] . P^T[32 tok][16 rows] per 16-dim tile,
-//       V^T from two transpose reads (tokens 4g.. and 16+4g.. of lane group g), P^T straight
-//       from the two score tiles.
-// K/V stream through the same 128 KB LDS ring (one barrier per block), laid out with dswz.
-template <int HD, bool SHARED>
-__global__ __launch_bounds__(512, 1) void prefill16_kernel(PrefillArgs a) {
-    constexpr int kW = 8;                            // waves
-    constexpr int kT = kW * 64;                      // threads
-    constexpr int NKS = HD / 32;                     // K-steps of the score product (16x16x32)
-    constexpr int NDT = HD / 16;                     // 16-dim output tiles
-    constexpr int UNIT = kTok * HD * 2;              // bytes of the K (or V) of one block
-    constexpr int NU = kRingBytes / UNIT;            // ring depth in units
-    constexpr int LPU = UNIT / 16 / kT;              // 16-byte loads per lane per unit
-    constexpr int PAGE_BYTES = kPage * HD * 2;
-    constexpr int AHEAD = SHARED ? NU - 3 : NU - 4;
-    static_assert(AHEAD >= 0 && LPU % 2 == 0 && (NU - 1) * LPU + 1 <= 63, "ring shape");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c16 = lane & 15, g4 = lane >> 4;
-    const int g = a.group, Hq = a.num_q_heads;
-
-    // ---- XCD-aware work mapping (as in the four-wave kernel)
-    const int nwg = gridDim.x * gridDim.y * gridDim.z;
-    const int wid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int xcd = wid % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
-    const int item = xcd * per + min(xcd, extra) + wid / kXcds;
-    const int qt = gridDim.x - 1 - item % gridDim.x;
-    const int kvh = (item / gridDim.x) % gridDim.y;
-    const int b = item / (gridDim.x * gridDim.y);
-
-    const int q0 = a.cu_q[b], q_len = a.cu_q[b + 1] - q0;
-    const int L = a.ctx_lens[b];
-    const int BQ = kRows / g;
-    const int tile_q = qt * BQ;
-    if (q_len <= 0 || tile_q >= q_len)
-        return;
-    const int nq = min(BQ, q_len - tile_q);
-    const int p_first = L - q_len + tile_q;
-    const int p_last = p_first + nq - 1;
-    const bool bad_row = q_len > L || (L - 1) / kPage >= a.pt_stride;
-    const int lo = a.is_global ? 0 : max(0, p_first - a.window + 1);
-    const int kb0 = lo & ~(kTok - 1);
-    const int nblk = bad_row ? 0 : (p_last - kb0) / kTok + 1;
-    const int pgA = kb0 / kPage;
-    const int npg = bad_row ? 0 : p_last / kPage - pgA + 1;
-    const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
-
-    // ---- this wave's rows: row m = 16 * wave + c16 is (query position m / g, head m % g)
-    const int m_own = 16 * wave + c16;
-    const int pos_own = m_own / g;
-    const bool ok_own = pos_own < nq;
-    const int p_own = p_first + pos_own;
-
-    // ---- Q^T as the B operand: lane holds row c16, dims 32 s + 8 g4 .. +7
-    u32x4 qb[NKS];
-    {
-        const uint16_t *qp =
-            a.q + ((int64_t)(q0 + tile_q + (ok_own ? pos_own : 0)) * Hq + kvh * g + m_own % g) * HD + 8 * g4;
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            const u32x4 v = *(const u32x4 *)(qp + 32 * s);
-            qb[s] = ok_own ? v : u32x4{0, 0, 0, 0};
-        }
-    }
-
-    f32x4 acc[NDT];
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-        acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f, l_ex = 0.f;
-    int bad_page = 0;
-
-    // ---- ring fill: load k of a unit writes LDS chunk position P = k*512 + wave*64 + lane,
-    // i.e. token row P / (HD/8) of the block, slot P % (HD/8); it fetches the chunk dswz puts
-    // there. Loads 0 .. LPU/2-1 cover the block's first page, the rest its second.
-    auto src_off = [&](int k) {
-        const int P = k * kT + wave * 64 + lane;
-        const int t = P / (HD / 8);
-        const int c = (P % (HD / 8)) ^ dswz(t & 15);
-        return (uint32_t)((t & 15) * HD + c * 8) * 2u;
-    };
-    auto load_ids = [&](int first) {
-        return bad_row ? 0 : pt[pgA + min(first + lane, max(npg - 1, 0))];
-    };
-    int ids = load_ids(0), ids_next = load_ids(64);
-    int ids_base = 0;
-    const uint32_t npages32 = (uint32_t)min<int64_t>(a.num_pages, INT32_MAX);
-    const uint64_t kbase = (uint64_t)(uintptr_t)(a.k_pool + (int64_t)kvh * kPage * HD);
-    const uint64_t vbase = (uint64_t)(uintptr_t)(a.v_pool + (int64_t)kvh * kPage * HD);
-    const uint64_t page_stride = (uint64_t)a.num_kv_heads * PAGE_BYTES;
-    // Units in the order of first use (see the four-wave kernel).
-    auto issue = [&](int u) {
-        const int blk = SHARED ? u : (u == 0 ? 0 : ((u & 1) ? (u + 1) >> 1 : (u >> 1) - 1));
-        const bool is_v = !SHARED && u > 0 && (u & 1) == 0;
-        if (blk < nblk && 2 * blk + 1 - ids_base >= 96) {
-            ids = ids_next;
-            ids_base += 64;
-            ids_next = load_ids(ids_base + 64);
-        }
-        const uint64_t base = is_v ? vbase : kbase;
-        u32x4 rs[2];
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const int rel = 2 * blk + pp;
-            const int pg = pgA + rel;
-            const bool in_range = blk < nblk && pg * kPage <= p_last && pg * kPage + kPage - 1 >= lo;
-            const int r = (rel - ids_base) & 127;
-            const int id_a = __builtin_amdgcn_readlane(ids, r & 63);
-            const int id_b = __builtin_amdgcn_readlane(ids_next, r & 63);
-            const uint32_t pid = (uint32_t)(r >= 64 ? id_b : id_a);
-            const bool valid = pid < npages32;
-            const bool live = in_range && valid;
-            bad_page |= (int)(in_range && !valid);
-            const uint64_t addr = base + (uint64_t)(live ? pid : 0u) * page_stride;
-            rs[pp] = u32x4{(uint32_t)addr, (uint32_t)(addr >> 32) & 0xFFFFu, live ? (uint32_t)PAGE_BYTES : 0u,
-                           0x00020000u};
-        }
-        const uint32_t dst = (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT) + (uint32_t)(wave * 64 * 16);
-#pragma unroll
-        for (int k = 0; k < LPU; ++k)
-            ring_load16(rs[k < LPU / 2 ? 0 : 1], dst + k * kT * 16, src_off(k));
-    };
-    auto unit_k = [&](int j) { return SHARED ? j : (j == 0 ? 0 : 2 * j - 1); };
-    auto unit_v = [&](int j) { return SHARED ? j : 2 * j + 2; };
-
-    // ---- per-lane LDS offsets
-    // K operand (key tile kt, step s): key 16 kt + c16, logical chunk 4 s + g4 ->
-    // kb[s % 4] + 256 (s / 4) + 16 kt * HD * 2 (the swizzle touches the low four chunk bits)
-    uint32_t kb[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-        kb[v] = (uint32_t)(c16 * HD * 2 + 16 * ((4 * v + g4) ^ dswz(c16)));
-    // V^T operand (dim tile dt, token half th): in 16-lane group g4, lane 4r + q supplies token
-    // 16 th + 4 g4 + r, dims 16 dt + 4q .. +3; the lane receives dim 16 dt + c16 of those four
-    // tokens -> vb[th][dt % 8] + 256 (dt / 8)
-    uint32_t vb[2][8];
-    {
-        const int r = c16 >> 2, q = c16 & 3;
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const int tok = 16 * th + 4 * g4 + r;
-                vb[th][d] = (uint32_t)(tok * HD * 2 + 16 * ((2 * d + (q >> 1)) ^ dswz(tok & 15)) + 8 * (q & 1));
-            }
-    }
-
-    const float scale = a.scale_log2;
-    // scores of block j: tile kt holds keys 16 kt + 4 g4 + i (i = 0..3) of row c16
-    auto qk = [&](int j, f32x4 (&st)[2]) {
-        const uint8_t *kst = ring + (unit_k(j) % NU) * UNIT;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NKS; s += 2) {
-                x = mfma_k32(*(const u32x4 *)(kst + kb[s & 3] + 256 * (s >> 2) + kt * 16 * HD * 2), qb[s], x);
-                y = mfma_k32(*(const u32x4 *)(kst + kb[(s + 1) & 3] + 256 * ((s + 1) >> 2) + kt * 16 * HD * 2),
-                             qb[s + 1], y);
-            }
-            st[kt] = x + y;
-        }
-    };
-    auto softmax = [&](int j, f32x4 (&st)[2], u32x4 &pf, float &alpha) {
-        const int T0 = kb0 + j * kTok;
-        const int lim_hi = p_own - T0;
-        const int lim_lo = a.is_global ? INT32_MIN : p_own - a.window + 1 - T0;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = 16 * kt + 4 * g4 + i;
-                st[kt][i] = (o <= lim_hi && o >= lim_lo) ? st[kt][i] * scale : -INFINITY;
-                mx = fmaxf(mx, st[kt][i]);
-            }
-        const float m_new = fmaxf(m_run, rows_max4(mx));
-        const bool resc = m_new > m_run + kRescaleLog2;
-        alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
-        if (resc)
-            m_run = m_new;
-        const float mb = m_run == -INFINITY ? 0.f : m_run;
-        float ps[8];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ps[4 * kt + i] = fast_exp2(st[kt][i] - mb);
-        pf = u32x4{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3]), pack_bf16x2(ps[4], ps[5]),
-                   pack_bf16x2(ps[6], ps[7])};
-        float rs = 0.f, rx = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rs += bf16_lo(pf[i]) + bf16_hi(pf[i]);
-            rx += ps[2 * i] + ps[2 * i + 1];
-        }
-        l_run = l_run * alpha + rows_sum4(rs);
-        l_ex = l_ex * alpha + rows_sum4(rx);
-    };
-    auto pv = [&](int j, const u32x4 pf) {
-        const uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
-        const int T0 = kb0 + j * kTok;
-        // keep mask of the lane's eight tokens (all ones inside [lo, p_last])
-        u32x4 keep;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            uint32_t k = 0;
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2) {
-                const int e = 2 * w2 + r2;  // element: token 16 (e / 4) + 4 g4 + e % 4
-                const int T = T0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
-                k |= (T >= lo && T <= p_last) ? (r2 ? 0xFFFF0000u : 0x0000FFFFu) : 0u;
-            }
-            keep[w2] = k;
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint32_t o = 256 * (dt >> 3);
-            const u32x2 v0 = tr_read(vst + vb[0][dt & 7] + o);
-            const u32x2 v1 = tr_read(vst + vb[1][dt & 7] + o);
-            const u32x4 va = u32x4{v0[0], v0[1], v1[0], v1[1]} & keep;
-            acc[dt] = mfma_k32(va, pf, acc[dt]);
-        }
-    };
-
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int u = 0; u < NU - 1; ++u)
-        issue(u);
-    wait_vmcnt<(NU - 2) * LPU>();
-    __syncthreads();
-    f32x4 st[2];
-    u32x4 pf;
-    float alpha;
-    qk(0, st);
-    softmax(0, st, pf, alpha);
-
-    for (int j = 0; j < nblk; ++j) {
-        wait_vmcnt<AHEAD * LPU>();
-        __syncthreads();
-        if (SHARED) {
-            issue(j + NU - 1);
-        } else {
-            issue(2 * j + NU - 1);
-            issue(2 * j + NU);
-        }
-        // block nblk (computed in the last iteration) lies past every query: fully masked
-        f32x4 st1[2];
-        qk(j + 1, st1);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int d = 0; d < NDT; ++d)
-                acc[d] *= alpha;
-        }
-        u32x4 pf1;
-        float alpha1;
-        pv(j, pf);
-        softmax(j + 1, st1, pf1, alpha1);
-        pf = pf1;
-        alpha = alpha1;
-    }
-    wait_vmcnt<0>();
-
-    const bool bad = bad_row || __builtin_amdgcn_ballot_w64(bad_page) != 0;
-    if (!ok_own)
-        return;
-    const int64_t orow = (int64_t)(q0 + tile_q + pos_own) * Hq + kvh * g + m_own % g;
-    if (g4 == 0)
-        a.lse[orow] = bad ? __builtin_nanf("") : (m_run + fast_log2(l_ex)) * kLn2;
-    const float inv = 1.0f / l_run;
-    uint16_t *op = a.out + orow * HD + 4 * g4;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d) {
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = bad ? __builtin_nanf("") : acc[d][e] * inv;
-        *(u32x2 *)(op + 16 * d) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
-}
-
-// head_dim 256 runs the eight-wave kernel (its registers allow two waves per SIMD); head_dim
-// 512 needs the whole register file of a SIMD for one wave's 32 rows and runs the four-wave
-// kernel. Both were measured on the mixed-step prefill rows of their family.
 template <int HD, bool SHARED>
 hipError_t launch(const PrefillArgs &a, dim3 grid, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    if constexpr (HD == 256)
-        return hipLaunchKernel((const void *)prefill16_kernel<HD, SHARED>, grid, dim3(512), args, 0, stream);
-    else
-        return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel((const void *)prefill_kernel<HD, SHARED>, grid, dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
