@@ -43,11 +43,18 @@ def parse():
 
 
 def kernel_source_digest():
+    """Digest of the decode path's code (comments and blank lines dropped, so that a change of
+    wording does not invalidate the committed counters)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("decode.hip", "common.h", "combine.hip"):
-        with open(os.path.join(ROOT, "global_paged_gqa_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "global_paged_gqa_amd", "csrc", f)) as fh:
+            src = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in src.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
