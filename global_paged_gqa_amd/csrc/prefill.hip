@@ -49,7 +49,9 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 128;          // MFMA rows per workgroup (4 tiles of 32)
+// MFMA rows per wave: two 32-row tiles at head_dim 256, one at 512 (the O accumulators fill
+// the AGPRs either way); the workgroup's four waves hold kWaves * 32 * row_tiles rows.
+constexpr int row_tiles(int hd) { return hd == 256 ? 2 : 1; }
 constexpr int kTok = 32;            // keys per block (two pages)
 constexpr int kRingBytes = 128 * 1024;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
@@ -91,6 +93,42 @@ __device__ __forceinline__ void qk4(f32x16 &st, u32x4 k0, u32x4 k1, u32x4 k2, u3
             : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(q0), "v"(q1), "v"(q2), "v"(q3));
 }
 
+// Two K-steps of the score product (as qk4).
+template <bool first>
+__device__ __forceinline__ void qk2(f32x16 &st, u32x4 k0, u32x4 k1, u32x4 q0, u32x4 q1) {
+    if (first)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
+            : "=&v"(st)
+            : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
+            : "+v"(st)
+            : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+}
+
+// Two K-steps for two row tiles (A shared, B per tile), the tiles' MFMAs alternating so that
+// no MFMA depends on the one issued just before it.
+template <bool first>
+__device__ __forceinline__ void qk2x2(f32x16 &s0, f32x16 &s1, u32x4 k0, u32x4 k1, u32x4 a0, u32x4 a1, u32x4 b0,
+                                      u32x4 b1) {
+    if (first)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %1, %2, %6, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %5, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %1, %3, %7, %1"
+            : "=&v"(s0), "=&v"(s1)
+            : "v"(k0), "v"(k1), "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %1, %2, %6, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %5, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %1, %3, %7, %1"
+            : "+v"(s0), "+v"(s1)
+            : "v"(k0), "v"(k1), "v"(a0), "v"(a1), "v"(b0), "v"(b1));
+}
+
 // The wait states an MFMA result needs before a vector instruction may read it (the
 // compiler cannot see that qk4 is an MFMA), with margin.
 __device__ __forceinline__ void qk_settle(f32x16 &st) {
@@ -117,6 +155,19 @@ __device__ __forceinline__ void scale_acc(f32x16 &c, float al) {
         c[v + 2] = x2;
         c[v + 3] = x3;
     }
+}
+
+// Helpers for the rare paths of the block loop (window slides, edge blocks): the lane index
+// recomputed and zeros made on the spot, so that the compiler keeps neither live across the
+// loop (spilled, their reloads would wait on the ring's loads).
+__device__ __forceinline__ int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ __forceinline__ u32x4 fresh_zeros() {
+    uint32_t a, b, c, d;
+    asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                 : "=v"(a), "=v"(b), "=v"(c), "=v"(d));
+    return u32x4{a, b, c, d};
 }
 
 // Page resources of one tile's K/V stream. A ring unit is the K (or V) of one 32-token block,
@@ -153,12 +204,12 @@ struct TilePages {
         bad = 0;
     }
     // buffer resource of this wave's page of block blk in the K or V pool
-    __device__ u32x4 rsrc(int blk, bool is_v, int wave, int lane) {
+    __device__ u32x4 rsrc(int blk, bool is_v, int wave) {
         const int rel = 2 * blk + wave / WPP;
         if (rel < npg && rel - ids_base >= 96) {
             ids = ids_next;
             ids_base += 64;
-            ids_next = load_ids(ids_base + 64, lane);
+            ids_next = load_ids(ids_base + 64, lane_id());
             // Wait for the ids here, on this rare path. Left to the compiler, the wait lands
             // after the branch, on every call, and drains the ring loads in flight each time.
             __builtin_amdgcn_s_waitcnt(0);
@@ -184,6 +235,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     constexpr int NU = kRingBytes / UNIT;            // ring depth in units
     constexpr int LPU = UNIT / 16 / kThreads;        // 16-byte loads per lane per unit
     constexpr int PAGE_BYTES = kPage * HD * 2;       // one (page, KV head) block
+    constexpr int RT = row_tiles(HD);                // 32-row tiles per wave
+    constexpr int kRows = kWaves * 32 * RT;          // MFMA rows per workgroup
     // K = V: units that may still be in flight when an iteration starts (the ones it reads have
     // landed). Separate pools keep four units in the ring (two read, two in flight).
     constexpr int AHEAD = NU - 3;
@@ -228,32 +281,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int pgA = kb0 / kPage;                                         // first page of block 0
     const int npg = bad_row ? 0 : p_last / kPage - pgA + 1;
 
-    // ---- this wave's rows: row m = 32 * wave + n32 is (query position m / g, head m % g)
-    const int m_own = 32 * wave + n32;
-    const int pos_own = m_own / g;
-    const bool ok_own = pos_own < nq;
-    const int p_own = p_first + pos_own;
+    // ---- this wave's rows: tile r holds rows m = 32 (RT wave + r) + n32, each (query position
+    // m / g, head m % g)
+    auto m_own = [&](int r) { return 32 * (RT * wave + r) + n32; };
+    auto pos_own = [&](int r) { return m_own(r) / g; };
+    auto ok_own = [&](int r) { return pos_own(r) < nq; };
+    int p_own[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+        p_own[r] = p_first + pos_own(r);
 
     // ---- Q^T as the B operand: lane holds row n32, dims 16 s + 8 h .. +7 (zeros for padding rows)
-    u32x4 qb[NKS];
-    {
+    u32x4 qb[RT][NKS];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
         const uint16_t *qp =
-            a.q + ((int64_t)(q0 + tile_q + (ok_own ? pos_own : 0)) * Hq + kvh * g + m_own % g) * HD + 8 * h;
+            a.q + ((int64_t)(q0 + tile_q + (ok_own(r) ? pos_own(r) : 0)) * Hq + kvh * g + m_own(r) % g) * HD + 8 * h;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const u32x4 v = *(const u32x4 *)(qp + 16 * s);
-            qb[s] = ok_own ? v : u32x4{0, 0, 0, 0};
+            qb[r][s] = ok_own(r) ? v : u32x4{0, 0, 0, 0};
         }
     }
 
-    // O^T tiles of this wave's 32 rows over the whole head dimension (AGPRs)
-    f32x16 acc[NDT];
+    // O^T tiles of this wave's rows over the whole head dimension (AGPRs)
+    f32x16 acc[RT][NDT];
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[d][v] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f, l_ex = 0.f;
+        for (int d = 0; d < NDT; ++d)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[r][d][v] = 0.f;
+    float m_run[RT], l_run[RT], l_ex[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        m_run[r] = -INFINITY;
+        l_run[r] = 0.f;
+        l_ex[r] = 0.f;
+    }
 
     // ---- ring fill. Wave w loads page w / 2 of each unit: its load k writes the unit's LDS
     // chunk position P = 1024 (w / 2) + 128 k + 64 (w % 2) + lane, i.e. token row P / (HD/8) of
@@ -282,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto prep = [&](int u) {
         const int blk = SHARED ? u : (u == 0 ? 0 : ((u & 1) ? (u + 1) >> 1 : (u >> 1) - 1));
         const bool is_v = !SHARED && u > 0 && (u & 1) == 0;
-        return UnitLoad{pages.rsrc(blk, is_v, wave, lane), (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT)};
+        return UnitLoad{pages.rsrc(blk, is_v, wave), (uint32_t)(uintptr_t)(ring + (u % NU) * UNIT)};
     };
     auto emit = [&](const UnitLoad &ul, int k) { ring_load16(ul.rs, ul.dst + chunk0(k) * 16, src_off(k)); };
     auto issue = [&](int u) {
@@ -295,30 +361,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto unit_v = [&](int j) { return SHARED ? j : 2 * j + 2; };                // unit of block j's V
 
     // ---- per-lane LDS offsets of the operand reads
-    // K operand (step s): token n32, chunk 2s + h -> n32*HD*2 + 16*((2s + h) ^ swz) =
-    // kb[s & 7] + 256 * (s >> 3), the swizzle touching only the low 8 address bits.
-    uint32_t kb[8];
-    {
-        const int sw = swz(n32 & 15);
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-            kb[v] = (uint32_t)(n32 * HD * 2 + 16 * ((2 * v + h) ^ sw));
-    }
+    // K operand (step s): token n32, chunk 2s + h -> n32*HD*2 + 16*((2s + h) ^ swz); with
+    // v = s & 7 that is krow + ((32 v) ^ kx) + 256 (s >> 3), kx = 16 (h ^ swz) (the swizzle
+    // touches only the low 8 address bits), one XOR per read instead of eight offsets held.
+    const uint32_t krow = (uint32_t)(n32 * HD * 2);
+    const uint32_t kx = (uint32_t)(16 * (h ^ swz(n32 & 15)));
     // V^T operand (transpose read i of dim tile dt, page p): in 16-lane group G (G&1: dims
     // 16..31 of the tile, G>>1 = h), lane 4r + q supplies token 16p + 8i + 4h + r, dims 4q .. 4q+3
-    // of its 16; the lane receives its dim for those four tokens. The offset repeats every four
-    // tiles (256 bytes): vb[i][dt & 3] + 256 * (dt >> 2).
-    uint32_t vb[2][4];
+    // of its 16; the lane receives its dim for those four tokens. Its chunk 4 (dt & 3) + k,
+    // k = 2 (G&1) + q/2, lands at slot (4 (dt & 3)) ^ (k ^ swz(token)), so the offset is
+    // vrow[i] + ((64 (dt & 3)) ^ vx[i]) + 256 (dt >> 2).
+    uint32_t vrow[2], vx[2];
     {
         const int G = lane >> 4, gh = G & 1, r = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int tok = 8 * i + 4 * h + r;
-                const int c = 4 * d + 2 * gh + (q >> 1);
-                vb[i][d] = (uint32_t)(tok * HD * 2 + 16 * (c ^ swz(tok)) + 8 * (q & 1));
-            }
+        for (int i = 0; i < 2; ++i) {
+            const int tok = 8 * i + 4 * h + r;
+            vrow[i] = (uint32_t)(tok * HD * 2 + 8 * (q & 1));
+            vx[i] = (uint32_t)(16 * ((2 * gh + (q >> 1)) ^ swz(tok)));
+        }
     }
 
     const float scale = a.scale_log2;
@@ -326,29 +387,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // K-steps ahead of the MFMAs; the scheduling fences keep the compiler from hoisting every
     // read of the block (which would not fit beside Q in registers). hook(t) runs after group t
     // (ring loads issued between the MFMA groups).
-    auto qk = [&](int j, f32x16 &st, auto hook) {
+    // With two row tiles each K fragment feeds two MFMAs, so groups are two K-steps (the same
+    // MFMA time per group, half the fragment registers).
+    auto qk = [&](int j, f32x16 (&st)[RT], auto hook) {
+        constexpr int G = 4 / RT;  // K-steps per group
         const uint8_t *kst = ring + (unit_k(j) % NU) * UNIT;
-        auto kread = [&](int s) { return *(const u32x4 *)(kst + kb[s & 7] + 256 * (s >> 3)); };
-        u32x4 kf[2][4];
+        auto kread = [&](int s) {
+            return *(const u32x4 *)(kst + krow + ((32u * (s & 7)) ^ kx) + 256 * (s >> 3));
+        };
+        // KB fragment buffers: reads run KB - 1 groups ahead of their MFMAs
+        constexpr int KB = 2;
+        u32x4 kf[KB][G];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            kf[0][i] = kread(i);
+        for (int d = 0; d < KB - 1; ++d)
 #pragma unroll
-        for (int t = 0; t < NKS / 4; ++t) {
-            if (t + 1 < NKS / 4) {
+            for (int i = 0; i < G; ++i)
+                kf[d][i] = kread(G * d + i);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    kf[(t + 1) & 1][i] = kread(4 * (t + 1) + i);
+        for (int t = 0; t < NKS / G; ++t) {
+            if (t + KB - 1 < NKS / G) {
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    kf[(t + KB - 1) % KB][i] = kread(G * (t + KB - 1) + i);
             }
-            const u32x4 *kk = kf[t & 1];
-            if (t == 0)
-                qk4<true>(st, kk[0], kk[1], kk[2], kk[3], qb[0], qb[1], qb[2], qb[3]);
-            else
-                qk4<false>(st, kk[0], kk[1], kk[2], kk[3], qb[4 * t], qb[4 * t + 1], qb[4 * t + 2], qb[4 * t + 3]);
-            hook(t);
+            const u32x4 *kk = kf[t % KB];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const u32x4 *qq = qb[r] + G * t;
+                if constexpr (G == 4) {
+                    if (t == 0)
+                        qk4<true>(st[r], kk[0], kk[1], kk[2], kk[3], qq[0], qq[1], qq[2], qq[3]);
+                    else
+                        qk4<false>(st[r], kk[0], kk[1], kk[2], kk[3], qq[0], qq[1], qq[2], qq[3]);
+                } else if (r == 0) {
+                    // both tiles at once, their MFMAs alternating
+                    const u32x4 *qr = qb[1] + G * t;
+                    if (t == 0)
+                        qk2x2<true>(st[0], st[1], kk[0], kk[1], qq[0], qq[1], qr[0], qr[1]);
+                    else
+                        qk2x2<false>(st[0], st[1], kk[0], kk[1], qq[0], qq[1], qr[0], qr[1]);
+                }
+            }
+            if ((t + 1) % RT == 0)
+                hook(t / RT);
             __builtin_amdgcn_sched_barrier(0);
         }
-        qk_settle(st);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+            qk_settle(st[r]);
     };
     // Masked online softmax of block j's scores for this wave's rows (lane holds tokens
     // 8(v/4) + 4h + v%4 of row n32; the other half of the row's 32 tokens is in lane n32 + 32).
@@ -363,75 +449,92 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // 11 the row sums' update.
     struct SmState {
         int lim_lo, lim_hi;
+        bool interior;  // every row of the tile sees all 32 keys of the block: no mask
         float mx, mb, rs, rx;
-        float ps[16];
     };
-    auto sm_init = [&](int j, SmState &z) {
+    auto sm_init = [&](int j, SmState &z, int r) {
         // visible iff T <= p_own (causal) and p_own - T < window (local): with the lane's token
         // offsets o(v) = 8(v/4) + 4h + v%4 from T0, that is lim_lo <= o(v) <= lim_hi
         const int T0 = kb0 + j * kTok;
-        z.lim_hi = p_own - T0;
-        z.lim_lo = a.is_global ? INT32_MIN : p_own - a.window + 1 - T0;
+        z.lim_hi = p_own[r] - T0;
+        z.lim_lo = a.is_global ? INT32_MIN : p_own[r] - a.window + 1 - T0;
+        z.interior = T0 + kTok - 1 <= p_first && (a.is_global || T0 >= p_last - a.window + 1);
         z.mx = -INFINITY;
         z.rs = 0.f;
         z.rx = 0.f;
     };
-    auto sm_step = [&](int step, SmState &z, f32x16 &st, u32x4 (&pf)[2], float &alpha) {
+    auto sm_step = [&](int step, SmState &z, f32x16 &st, u32x4 (&pf)[2], float &alpha, int r) {
         if (step < 4) {
+            if (z.interior) {
 #pragma unroll
-            for (int v = 4 * step; v < 4 * step + 4; ++v) {
-                const int o = 8 * (v >> 2) + 4 * h + (v & 3);
-                st[v] = (o <= z.lim_hi && o >= z.lim_lo) ? st[v] * scale : -INFINITY;
-                z.mx = fmaxf(z.mx, st[v]);
+                for (int v = 4 * step; v < 4 * step + 4; ++v) {
+                    st[v] *= scale;
+                    z.mx = fmaxf(z.mx, st[v]);
+                }
+            } else {
+#pragma unroll
+                for (int v = 4 * step; v < 4 * step + 4; ++v) {
+                    const int o = 8 * (v >> 2) + 4 * h + (v & 3);
+                    st[v] = (o <= z.lim_hi && o >= z.lim_lo) ? st[v] * scale : -INFINITY;
+                    z.mx = fmaxf(z.mx, st[v]);
+                }
             }
         } else if (step == 4) {
-            const float m_new = fmaxf(m_run, halves_max(z.mx));
-            const bool resc = m_new > m_run + kRescaleLog2;
-            alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
+            const float m_new = fmaxf(m_run[r], halves_max(z.mx));
+            const bool resc = m_new > m_run[r] + kRescaleLog2;
+            alpha = resc ? fast_exp2(m_run[r] - m_new) : 1.0f;
             if (resc)
-                m_run = m_new;
-            z.mb = m_run == -INFINITY ? 0.f : m_run;
+                m_run[r] = m_new;
+            z.mb = m_run[r] == -INFINITY ? 0.f : m_run[r];
         } else if (step < 9) {
 #pragma unroll
             for (int v = 4 * (step - 5); v < 4 * (step - 5) + 4; ++v)
-                z.ps[v] = fast_exp2(st[v] - z.mb);
+                st[v] = fast_exp2(st[v] - z.mb);  // the weights replace the scores
         } else if (step < 11) {
             const int q = step - 9;
-            pf[q] = u32x4{pack_bf16x2(z.ps[8 * q + 0], z.ps[8 * q + 1]), pack_bf16x2(z.ps[8 * q + 2], z.ps[8 * q + 3]),
-                          pack_bf16x2(z.ps[8 * q + 4], z.ps[8 * q + 5]), pack_bf16x2(z.ps[8 * q + 6], z.ps[8 * q + 7])};
+            pf[q] = u32x4{pack_bf16x2(st[8 * q + 0], st[8 * q + 1]), pack_bf16x2(st[8 * q + 2], st[8 * q + 3]),
+                          pack_bf16x2(st[8 * q + 4], st[8 * q + 5]), pack_bf16x2(st[8 * q + 6], st[8 * q + 7])};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 z.rs += bf16_lo(pf[q][i]) + bf16_hi(pf[q][i]);
-                z.rx += z.ps[8 * q + 2 * i] + z.ps[8 * q + 2 * i + 1];
+                z.rx += st[8 * q + 2 * i] + st[8 * q + 2 * i + 1];
             }
         } else if (step == 11) {
-            l_run = l_run * alpha + halves_sum(z.rs);
-            l_ex = l_ex * alpha + halves_sum(z.rx);
+            l_run[r] = l_run[r] * alpha + halves_sum(z.rs);
+            l_ex[r] = l_ex[r] * alpha + halves_sum(z.rx);
         }
     };
-    constexpr int SM_STEPS = 12;
-    auto softmax = [&](int j, f32x16 &st, u32x4 (&pf)[2], float &alpha) {
-        SmState z;
-        sm_init(j, z);
+    // step s of the RT row tiles' softmax: step s / RT of tile s % RT (the tiles' independent
+    // chains interleave)
+    constexpr int SM_STEPS = 12 * RT;
+    auto sm_any = [&](int s, SmState (&z)[RT], f32x16 (&st)[RT], u32x4 (&pf)[RT][2], float (&alpha)[RT]) {
+        const int r = s % RT;
+        sm_step(s / RT, z[r], st[r], pf[r], alpha[r], r);
+    };
+    auto softmax = [&](int j, f32x16 (&st)[RT], u32x4 (&pf)[RT][2], float (&alpha)[RT]) {
+        SmState z[RT];
 #pragma unroll
-        for (int step = 0; step < SM_STEPS; ++step)
-            sm_step(step, z, st, pf, alpha);
+        for (int r = 0; r < RT; ++r)
+            sm_init(j, z[r], r);
+#pragma unroll
+        for (int s = 0; s < SM_STEPS; ++s)
+            sm_any(s, z, st, pf, alpha);
     };
     // O^T += V^T P^T for block j over the whole head dimension, V^T fragments read one tile
     // ahead of the MFMAs. Tokens no row of the tile can see carry P = 0, and their V rows are
     // zeroed in LDS beforehand (clear_edge), so a never-written slot cannot turn 0 * V into a
     // NaN. hook(dt) runs after tile dt.
-    auto pv = [&](int j, const u32x4 pf0, const u32x4 pf1, auto hook) {
+    auto pv = [&](int j, const u32x4 (&pf)[RT][2], auto hook) {
         const uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
         auto vread = [&](int dt, int p) {
             const uint32_t o = 256 * (dt >> 2) + p * PAGE_BYTES;
-            const u32x2 v0 = tr_read(vst + vb[0][dt & 3] + o);
-            const u32x2 v1 = tr_read(vst + vb[1][dt & 3] + o);
+            const u32x2 v0 = tr_read(vst + vrow[0] + ((64u * (dt & 3)) ^ vx[0]) + o);
+            const u32x2 v1 = tr_read(vst + vrow[1] + ((64u * (dt & 3)) ^ vx[1]) + o);
             return u32x4{v0[0], v0[1], v1[0], v1[1]};
         };
         // fragments of tile dt in slot dt % PVA, read PVA - 1 tiles ahead of their MFMAs (the K
         // fragments of the score product are dead here, so the registers are free)
-        constexpr int PVA = 3;
+        constexpr int PVA = RT == 1 ? 3 : 2;
         u32x4 vf[PVA][2];
 #pragma unroll
         for (int d = 0; d < PVA - 1; ++d) {
@@ -444,8 +547,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 vf[(dt + PVA - 1) % PVA][0] = vread(dt + PVA - 1, 0);
                 vf[(dt + PVA - 1) % PVA][1] = vread(dt + PVA - 1, 1);
             }
-            acc[dt] = mfma32(vf[dt % PVA][0], pf0, acc[dt]);
-            acc[dt] = mfma32(vf[dt % PVA][1], pf1, acc[dt]);
+            // the two halves of the 32 tokens accumulate into the same tile: with two row tiles
+            // the four MFMAs alternate tiles, so no MFMA waits on the one just before it
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+                acc[r][dt] = mfma32(vf[dt % PVA][0], pf[r][0], acc[r][dt]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+                acc[r][dt] = mfma32(vf[dt % PVA][1], pf[r][1], acc[r][dt]);
             hook(dt);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -458,11 +567,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         if (T0 >= lo && T0 + kTok - 1 <= p_last)
             return false;
         uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
+        const u32x4 zero = fresh_zeros();
+        const int ln = lane_id();
         for (int t = wave; t < kTok; t += kWaves) {
             const int T = T0 + t;
             if (T < lo || T > p_last)
-                for (int c = lane; c < HD / 8; c += 64)
-                    *(u32x4 *)(vst + t * HD * 2 + c * 16) = u32x4{0, 0, 0, 0};
+                for (int c = ln; c < HD / 8; c += 64)
+                    *(u32x4 *)(vst + t * HD * 2 + c * 16) = zero;
         }
         return true;
     };
@@ -491,16 +602,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         issue(u);
     wait_vmcnt<(PRO - 1) * LPU>();  // unit 0 (the K of block 0) landed for this wave
     __syncthreads();
-    f32x16 st;
-    u32x4 pf[2];
-    float alpha;
+    f32x16 st[RT];
+    u32x4 pf[RT][2];
+    float alpha[RT];
     qk(0, st, no_hook);
     softmax(0, st, pf, alpha);
 
     // Iteration j: the scores of block j+1 (QK), then the PV product of block j interleaved by
     // the scheduler with the softmax of block j+1 (independent MFMA and VALU work).
     for (int j = 0; j < nblk; ++j) {
-        f32x16 st1;
+        f32x16 st1[RT];
         if (SHARED) {
             // unit j+1 landed for this wave; after the barrier for all waves, and unit j-1's slot
             // (read by the previous PV) is free
@@ -521,23 +632,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             qk(j + 1, st1, spread(ul, std::integral_constant<int, NKS / 4>{}));
         }
         // rescale this wave's rows for block j (factors from its softmax)
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-            for (int d = 0; d < NDT; ++d)
-                scale_acc(acc[d], alpha);
-        }
-        u32x4 pf1[2];
-        float alpha1;
-        SmState z;
-        sm_init(j + 1, z);
-        // PV tile dt is followed by softmax steps [dt S / NDT, (dt + 1) S / NDT) of the next block
+        for (int r = 0; r < RT; ++r)
+            if (__builtin_amdgcn_ballot_w64(alpha[r] != 1.0f)) {
+#pragma unroll
+                for (int d = 0; d < NDT; ++d)
+                    scale_acc(acc[r][d], alpha[r]);
+            }
+        u32x4 pf1[RT][2];
+        float alpha1[RT];
+        SmState z[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+            sm_init(j + 1, z[r], r);
+        // Softmax of the next block beside the PV tiles: the masking, maxima and exponentials
+        // (steps 0-8 of each row tile) spread over tiles 0 .. NDT-2, the packing into pf1 and
+        // the sums after the last tile, when pf is no longer read (pf1 can take its registers).
         auto sm_hook = [&](int dt) {
+            constexpr int E = 9 * RT;
+            if (dt < NDT - 1) {
 #pragma unroll
-            for (int step = dt * SM_STEPS / NDT; step < (dt + 1) * SM_STEPS / NDT; ++step)
-                sm_step(step, z, st1, pf1, alpha1);
+                for (int s = dt * E / (NDT - 1); s < (dt + 1) * E / (NDT - 1); ++s)
+                    sm_any(s, z, st1, pf1, alpha1);
+            } else {
+#pragma unroll
+                for (int s = E; s < SM_STEPS; ++s)
+                    sm_any(s, z, st1, pf1, alpha1);
+            }
         };
         if (SHARED) {
-            pv(j, pf[0], pf[1], sm_hook);
+            pv(j, pf, sm_hook);
         } else {
             // the V of block j landed (units 2j+3 and 2j+4 may be in flight); after the barrier
             // for all waves, and the slot of block j+1's K (read by the QK above) is free
@@ -547,14 +671,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 __syncthreads();
             const UnitLoad ul = prep(2 * j + 5);
             auto loads = spread(ul, std::integral_constant<int, NDT>{});
-            pv(j, pf[0], pf[1], [&](int dt) {
+            pv(j, pf, [&](int dt) {
                 loads(dt);
                 sm_hook(dt);
             });
         }
-        pf[0] = pf1[0];
-        pf[1] = pf1[1];
-        alpha = alpha1;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            pf[r][0] = pf1[r][0];
+            pf[r][1] = pf1[r][1];
+            alpha[r] = alpha1[r];
+        }
     }
 
     // No ring load (the zero-filling ones past the last block included) may still be writing
@@ -570,23 +697,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
     // ---- this wave's rows: normalise and write O, LSE
     const bool bad = bad_row || bad_tile(pages.bad);
-    if (!ok_own)
-        return;
-    const int64_t orow = (int64_t)(q0 + tile_q + pos_own) * Hq + kvh * g + m_own % g;
-    if (h == 0)
-        a.lse[orow] = bad ? __builtin_nanf("") : (m_run + fast_log2(l_ex)) * kLn2;
-    const float inv = 1.0f / l_run;
-    uint16_t *op = a.out + orow * HD + 4 * h;
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+    for (int r = 0; r < RT; ++r) {
+        if (!ok_own(r))
+            continue;
+        const int64_t orow = (int64_t)(q0 + tile_q + pos_own(r)) * Hq + kvh * g + m_own(r) % g;
+        if (h == 0)
+            a.lse[orow] = bad ? __builtin_nanf("") : (m_run[r] + fast_log2(l_ex[r])) * kLn2;
+        const float inv = 1.0f / l_run[r];
+        uint16_t *op = a.out + orow * HD + 4 * h;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            float o[4];
+        for (int d = 0; d < NDT; ++d)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = bad ? __builtin_nanf("") : acc[d][4 * jj + e] * inv;
-            *(u32x2 *)(op + 32 * d + 8 * jj) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        }
+            for (int jj = 0; jj < 4; ++jj) {
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = bad ? __builtin_nanf("") : acc[r][d][4 * jj + e] * inv;
+                *(u32x2 *)(op + 32 * d + 8 * jj) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            }
+    }
 }
 
 template <int HD, bool SHARED>
@@ -598,7 +728,7 @@ hipError_t launch(const PrefillArgs &a, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, bool kv_shared, int batch, hipStream_t stream) {
-    const int bq = kRows / a.group;
+    const int bq = kWaves * 32 * row_tiles(head_dim) / a.group;  // query positions per tile
     const dim3 grid((a.max_q + bq - 1) / bq, a.num_kv_heads, batch);
     if (head_dim == 256)
         return kv_shared ? launch<256, true>(a, grid, stream) : launch<256, false>(a, grid, stream);
