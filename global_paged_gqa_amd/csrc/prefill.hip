@@ -366,6 +366,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // touches only the low 8 address bits), one XOR per read instead of eight offsets held.
     const uint32_t krow = (uint32_t)(n32 * HD * 2);
     const uint32_t kx = (uint32_t)(16 * (h ^ swz(n32 & 15)));
+    // One row tile leaves registers for the eight offsets themselves (no VALU work per read);
+    // two row tiles need those registers and compute the XOR per read.
+    uint32_t ktab[RT == 1 ? 8 : 1];
+    if constexpr (RT == 1) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+            ktab[v] = krow + ((32u * v) ^ kx);
+    }
+    auto koff = [&](int s) -> uint32_t {
+        if constexpr (RT == 1)
+            return ktab[s & 7] + 256 * (s >> 3);
+        else
+            return krow + ((32u * (s & 7)) ^ kx) + 256 * (s >> 3);
+    };
     // V^T operand (transpose read i of dim tile dt, page p): in 16-lane group G (G&1: dims
     // 16..31 of the tile, G>>1 = h), lane 4r + q supplies token 16p + 8i + 4h + r, dims 4q .. 4q+3
     // of its 16; the lane receives its dim for those four tokens. Its chunk 4 (dt & 3) + k,
@@ -381,6 +395,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             vx[i] = (uint32_t)(16 * ((2 * gh + (q >> 1)) ^ swz(tok)));
         }
     }
+    uint32_t vtab[2][RT == 1 ? 4 : 1];
+    if constexpr (RT == 1) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                vtab[i][d] = vrow[i] + ((64u * d) ^ vx[i]);
+    }
+    // offset of transpose read i of tile dt within its 256-byte group of four tiles
+    auto voff = [&](int i, int dt) -> uint32_t {
+        if constexpr (RT == 1)
+            return vtab[i][dt & 3];
+        else
+            return vrow[i] + ((64u * (dt & 3)) ^ vx[i]);
+    };
 
     const float scale = a.scale_log2;
     // S^T[32 tok][32 rows] of block j for this wave's rows. Operand reads run one group of four
@@ -393,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         constexpr int G = 4 / RT;  // K-steps per group
         const uint8_t *kst = ring + (unit_k(j) % NU) * UNIT;
         auto kread = [&](int s) {
-            return *(const u32x4 *)(kst + krow + ((32u * (s & 7)) ^ kx) + 256 * (s >> 3));
+            return *(const u32x4 *)(kst + koff(s));
         };
         // KB fragment buffers: reads run KB - 1 groups ahead of their MFMAs
         constexpr int KB = 2;
@@ -528,8 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         const uint8_t *vst = ring + (unit_v(j) % NU) * UNIT;
         auto vread = [&](int dt, int p) {
             const uint32_t o = 256 * (dt >> 2) + p * PAGE_BYTES;
-            const u32x2 v0 = tr_read(vst + vrow[0] + ((64u * (dt & 3)) ^ vx[0]) + o);
-            const u32x2 v1 = tr_read(vst + vrow[1] + ((64u * (dt & 3)) ^ vx[1]) + o);
+            const u32x2 v0 = tr_read(vst + voff(0, dt) + o);
+            const u32x2 v1 = tr_read(vst + voff(1, dt) + o);
             return u32x4{v0[0], v0[1], v1[0], v1[1]};
         };
         // fragments of tile dt in slot dt % PVA, read PVA - 1 tiles ahead of their MFMAs (the K
