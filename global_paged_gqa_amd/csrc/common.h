@@ -36,8 +36,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two fp32 values to a bf16 pair (low, high), round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // The bf16 values in the low / high half of a packed pair, widened exactly to fp32.
