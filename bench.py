@@ -105,30 +105,45 @@ def cpu_baseline(batch, kv_bytes):
 
 
 def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
+    """The mixed step of each family: its 4 prefill chunks alone (TFLOP/s), its 60 decode rows
+    alone (GB/s) and the whole step, gattn_prefill then gattn_decode on one stream. Every timed
+    run follows a 1 GiB write that flushes the MALL, outside the events."""
     out = {}
-    for fam in ("global", "local"):
-        pre, _ = workloads.cfg4_mixed(fam)
-        d = devio.DeviceBatch(pre)
-        d.prefill()
-        torch.cuda.synchronize()
-        s = pre.spec
-        flops = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens, pre.q_lens)
+
+    def timed(fn):
         ts = []
         for _ in range(iters):
             flush.zero_()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            d.prefill()
+            fn()
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
-        ts.sort()
-        t = ts[len(ts) // 2]
+        return median(ts)
+
+    for fam in ("global", "local"):
+        pre, dec = workloads.cfg4_mixed(fam)
+        d = devio.DeviceBatch(pre)
+        dd = devio.DeviceBatch(dec)
+        d.prefill()
+        dd.decode(512)
+        torch.cuda.synchronize()
+        s = pre.spec
+        flops = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens, pre.q_lens)
+        kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, dec.ctx_lens)
+        t = timed(d.prefill)
+        td = timed(lambda: dd.decode(512))
+        tstep = timed(lambda: (d.prefill(), dd.decode(512)))
         tf = flops / t / 1e12
         out[fam] = {"tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                     "ms": round(t * 1e3, 4), "flops": flops,
-                    "workload": f"{fam}: 4 chunks x 2048 queries, priors {pre.ctx_lens.tolist()}"}
-        del d
+                    "decode_rows_us": round(td * 1e6, 2), "decode_rows_kv_bytes": kv,
+                    "decode_rows_gbs": round(kv / td / 1e9, 1),
+                    "step_ms": round(tstep * 1e3, 4),
+                    "workload": f"{fam}: 4 chunks x 2048 queries, priors {pre.ctx_lens.tolist()}; "
+                                f"60 decode rows, contexts ~U{{1..8192}}, split 512"}
+        del d, dd
     return out
 
 
