@@ -37,8 +37,8 @@
 // query] (the sliding-window tile pruning of the vllm-gemma-4-31b skills page, "Three
 // load-bearing facts", first item); pages in a
 // block that lie outside it are never read (zero-size buffer resource: zeros, no traffic).
-// Workgroups are mapped so that each XCD works through the query tiles of the same (row,
-// KV head), heaviest first, sharing that XCD's L2.
+// Workgroups take the query tiles of each (row, KV head) heaviest first, dealt round-robin over
+// the XCDs so that every XCD gets an equal share of every row.
 #include "common.h"
 #include "kernels.h"
 
@@ -46,7 +46,6 @@ namespace gattn {
 
 namespace {
 
-constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 // MFMA rows per wave: two 32-row tiles at head_dim 256, one at 512 (the O accumulators fill
@@ -250,13 +249,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int n32 = lane & 31, h = lane >> 5;
     const int g = a.group, Hq = a.num_q_heads;
 
-    // ---- XCD-aware work mapping: the dispatcher deals workgroups round-robin over the
-    // XCDs, so give XCD x a contiguous run of work items; within a (row, KV head) the query
-    // tiles run from the last (most keys) to the first.
-    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    // ---- work order: (row, KV head) pairs in turn, each pair's query tiles from the last (most
+    // keys) to the first. The dispatcher deals consecutive workgroups round-robin over the
+    // XCDs, so every XCD gets every eighth tile of each pair: equal shares of long and short
+    // rows, while an XCD's CUs still stream the K/V of the same one or two pairs through its L2.
+    // (Giving each XCD a contiguous run of pairs instead left the XCDs holding the longest rows
+    // working for a third longer than the rest.)
     const int wid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int xcd = wid % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
-    const int item = xcd * per + min(xcd, extra) + wid / kXcds;
+    const int item = wid;
     const int qt = gridDim.x - 1 - item % gridDim.x;
     const int kvh = (item / gridDim.x) % gridDim.y;
     const int b = item / (gridDim.x * gridDim.y);
