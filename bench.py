@@ -126,8 +126,10 @@ def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
         pre, dec = workloads.cfg4_mixed(fam)
         d = devio.DeviceBatch(pre)
         dd = devio.DeviceBatch(dec)
-        d.prefill()
-        dd.decode(512)
+        # warm-up: the first launches of a kernel run at a lower clock and miss its code caches
+        for _ in range(10):
+            d.prefill()
+            dd.decode(512)
         torch.cuda.synchronize()
         s = pre.spec
         flops = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens, pre.q_lens)

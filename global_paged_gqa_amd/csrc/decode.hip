@@ -40,31 +40,45 @@ namespace {
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-template <int HD, bool SHARED, int W, int kSliceBytes>
-__global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
-    // W waves, each an independent page stream through its own kSliceBytes of LDS
-    constexpr int kThreads = W * 64;
-    constexpr int kRingBytes = W * kSliceBytes;
-    constexpr int NKS = HD / 32;                 // K-steps of 32 dims in the score product
-    constexpr int NDT = HD / 16;                 // 16-dim output tiles in the PV product
-    constexpr int UNIT = kPage * HD * 2;         // bytes of one page's K (or V), one KV head
+template <int HD, bool SHARED, int W, int DS, int kSliceBytes>
+__global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a) {
+    // W page streams of DS waves each; a wave streams its share of the head dims of its
+    // stream's pages through its own kSliceBytes of LDS
+    constexpr int kWaves = W * DS;
+    constexpr int kThreads = kWaves * 64;
+    constexpr int kRingBytes = kWaves * kSliceBytes;
+    constexpr int NKS = HD / 32 / DS;            // K-steps of 32 dims in the wave's score partial
+    constexpr int NDT = HD / 16 / DS;            // 16-dim output tiles of the wave
+    constexpr int SEG = HD / DS;                 // head dims per wave
+    constexpr int SEGB = SEG * 2;                // bytes of a token row's segment
+    constexpr int PAGEB = kPage * HD * 2;        // bytes of one page's K (or V), one KV head
+    constexpr int UNIT = kPage * SEGB;           // the wave's segment of it
     constexpr int UPP = SHARED ? 1 : 2;          // units per page
     constexpr int SUB = kSliceBytes;
     constexpr int NU = SUB / UNIT;               // units in a slice
     constexpr int LPU = UNIT / 1024;             // 1 KB load instructions per unit
-    constexpr int CPR = HD / 8;                  // 16-byte chunks per token row
+    constexpr int CPR = SEG / 8;                 // 16-byte chunks per segment row
+    // The score of a page is always formed as NCH partial products over consecutive quarters
+    // (halves at head_dim 256) of the head dims, added in a fixed tree, whatever DS is: a wave
+    // holds NCH / DS of them, so the sum, and everything after it, has the same bits for any DS.
+    constexpr int NCH = HD == 512 ? 4 : 2;
+    constexpr int CPW = NCH / DS;                // partial chains per wave
+    static_assert(NCH % DS == 0 && (DS == 1 || W == 1), "dims split shape");
+    static_assert(CPR >= 16 && LPU >= 1, "segment shape");
     static_assert(NU >= 2, "decode ring shape");
     static_assert(NU * LPU + 1 <= 63, "vmcnt range");
-    static_assert(16 * HD * 4 <= kSliceBytes, "merge buffer");
+    static_assert(16 * HD * 4 <= DS * kSliceBytes, "merge buffer");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
     __shared__ float sm_m[W][16];
     __shared__ float sm_l[W][16];   // row sums of the bf16 weights (normalise O)
     __shared__ float sm_lx[W][16];  // row sums of the fp32 weights (LSE)
     __shared__ int sm_bad[W];
+    __shared__ f32x4 sm_part[2][DS][64];  // score partials of the dim-split waves (double buffer)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pw = wave / DS, dq = wave % DS;  // page stream, head-dim segment
     const int c16 = lane & 15;  // MFMA row/column index of this lane
     const int r4 = lane >> 4;   // 16-lane row of this lane
     const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -91,22 +105,22 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     }
     const int pg0 = tb / kPage;
     const int npg = bad_len ? 0 : (te - 1) / kPage - pg0 + 1;
-    const int my_pages = npg > wave ? (npg - wave + W - 1) / W : 0;  // this wave's: w, w+W, ...
+    const int my_pages = npg > pw ? (npg - pw + W - 1) / W : 0;  // this stream's: w, w+W, ...
     const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
     const int pg_hi = npg > 0 ? pg0 + npg - 1 : pg0;  // last table entry this workgroup may read
 
     // ---- this wave's page ids, 64 at a time in one vector register (lane j: the wave's page
     // 64k + j), read back with readlane when a page is issued. Indices past the split are
     // clamped to an entry the workgroup owns (their ids are never used).
-    auto load_ids = [&](int first) { return pt[min(pg0 + (first + lane) * W + wave, pg_hi)]; };
+    auto load_ids = [&](int first) { return pt[min(pg0 + (first + lane) * W + pw, pg_hi)]; };
     int ids = load_ids(0), ids_next = load_ids(64);
     int ids_base = 0;
 
     // ---- Q^T as the B operand of the score product: lane holds head c16 (zeros past g),
-    // dims 32 s + 8 r4 .. +7
+    // dims SEG dq + 32 s + 8 r4 .. +7
     u32x4 qb[NKS];
     {
-        const uint16_t *qp = a.q + ((int64_t)b * Hq + kvh * g + min(c16, g - 1)) * HD + 8 * r4;
+        const uint16_t *qp = a.q + ((int64_t)b * Hq + kvh * g + min(c16, g - 1)) * HD + SEG * dq + 8 * r4;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             const u32x4 v = *(const u32x4 *)(qp + 32 * s);
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     uint32_t kbase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        kbase[j] = (uint32_t)(c16 * HD * 2 + ((4 * j + r4) ^ dswz(c16)) * 16);
+        kbase[j] = (uint32_t)(c16 * SEGB + ((4 * j + r4) ^ dswz(c16)) * 16);
     // V^T operand (dim tile dt): in 16-lane group r4, lane 4r + q supplies token 4 r4 + r,
     // dims 16 dt + 4q .. +3; the lane receives dim 16 dt + c16 of those four tokens.
     // -> vbase[dt % 8] + 256 (dt / 8)
@@ -130,15 +144,15 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
         const int t = 4 * r4 + (c16 >> 2), q = c16 & 3;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            vbase[j] = (uint32_t)(t * HD * 2 + ((2 * j + (q >> 1)) ^ dswz(t)) * 16 + 8 * (q & 1));
+            vbase[j] = (uint32_t)(t * SEGB + ((2 * j + (q >> 1)) ^ dswz(t)) * 16 + 8 * (q & 1));
     }
     // ring fill: instruction i of a unit writes lane's 16 bytes to the slice's chunk position
     // P = 64 i + lane, which holds token P / CPR at chunk slot P % CPR, i.e. that token's chunk
-    // (slot ^ dswz(token)) of the page block.
+    // (slot ^ dswz(token)) of the wave's segment of the page block.
     auto src_off = [&](int i) {
         const int P = 64 * i + lane;
         const int t = P / CPR;
-        return (uint32_t)(t * CPR + ((P % CPR) ^ dswz(t))) * 16u;
+        return (uint32_t)(t * HD * 2 + SEGB * dq + ((P % CPR) ^ dswz(t)) * 16);
     };
 
     f32x4 acc[NDT];
@@ -171,7 +185,7 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
         if (!live)
             pid = 0;
         const uint16_t *pool = (SHARED || (u & 1) == 0) ? a.k_pool : a.v_pool;
-        const u32x4 rs = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD), live ? UNIT : 0);
+        const u32x4 rs = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD), live ? PAGEB : 0);
         const uint32_t dst = sub_lds + (uint32_t)((u % NU) * UNIT);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -188,19 +202,42 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
 
     int u = 0;
     for (int k = 0; k < my_pages; ++k) {
-        const int t0 = (pg0 + k * W + wave) * kPage;
+        const int t0 = (pg0 + k * W + pw) * kPage;
         // ---- K unit u landed once at most the NU - 1 later units' loads are outstanding
         wait_vmcnt<(NU - 1) * LPU>();
         const uint8_t *ks = sub + (u % NU) * UNIT;
-        f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+        // this wave's partial chains (chain c: its K-steps [c NKS/CPW, (c+1) NKS/CPW)), their
+        // steps interleaved so that consecutive MFMAs are independent
+        f32x4 ch[CPW];
 #pragma unroll
-        for (int s = 0; s < NKS; s += 2) {
-            st0 = mfma_k32(*(const u32x4 *)(ks + kbase[s & 3] + 256 * (s >> 2)), qb[s], st0);
-            st1 = mfma_k32(*(const u32x4 *)(ks + kbase[(s + 1) & 3] + 256 * ((s + 1) >> 2)), qb[s + 1], st1);
-        }
-        f32x4 st = st0 + st1;
+        for (int c = 0; c < CPW; ++c)
+            ch[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NKS / CPW; ++i)
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const int s = c * (NKS / CPW) + i;
+                ch[c] = mfma_k32(*(const u32x4 *)(ks + kbase[s & 3] + 256 * (s >> 2)), qb[s], ch[c]);
+            }
+        f32x4 st;
+        if constexpr (CPW == 4)
+            st = (ch[0] + ch[1]) + (ch[2] + ch[3]);
+        else if constexpr (CPW == 2)
+            st = ch[0] + ch[1];
+        else
+            st = ch[0];
         if (!SHARED)
             issue(u + NU);
+        if constexpr (DS > 1) {
+            // the DS partials meet in LDS; every wave adds them in the same tree
+            sm_part[k & 1][dq][lane] = st;
+            __syncthreads();
+            const f32x4 p0 = sm_part[k & 1][0][lane], p1 = sm_part[k & 1][1][lane];
+            if constexpr (DS == 4)
+                st = (p0 + p1) + (sm_part[k & 1][2][lane] + sm_part[k & 1][3][lane]);
+            else
+                st = p0 + p1;
+        }
 
         // ---- online softmax; lane holds S^T[token t0 + 4 r4 + e][head c16]. Tokens outside
         // [tb, te) are selected out (a NaN in an unused slot never reaches the sums).
@@ -251,8 +288,8 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < kPage; ++r) {
                 const int t = t0 + r;
-                if ((t < tb || t >= te) && lane * 16 < HD * 2)
-                    *(u32x4 *)(vs + r * HD * 2 + lane * 16) = u32x4{0, 0, 0, 0};
+                if ((t < tb || t >= te) && lane * 16 < SEGB)
+                    *(u32x4 *)(vs + r * SEGB + lane * 16) = u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -265,17 +302,19 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     // writing LDS when the slices are reused below.
     wait_vmcnt<0>();
 
-    // ---- merge the wave states (fixed order) and write this split's result
+    // ---- merge the page streams' states (fixed order) and write this split's result. The DS
+    // waves of a stream hold the same softmax state (the same arithmetic on the same scores)
+    // and each contributes its head dims.
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad_page) != 0;
-    if (lane == 0)
-        sm_bad[wave] = wave_bad;
-    if (r4 == 0) {
-        sm_m[wave][c16] = m_run;
-        sm_l[wave][c16] = l_run;
-        sm_lx[wave][c16] = l_ex;
+    if (lane == 0 && dq == 0)
+        sm_bad[pw] = wave_bad;
+    if (r4 == 0 && dq == 0) {
+        sm_m[pw][c16] = m_run;
+        sm_l[pw][c16] = l_run;
+        sm_lx[pw][c16] = l_ex;
     }
     __syncthreads();  // every wave is done with its slice; the states are visible
-    float *const mo = (float *)ring;  // [W][g][HD] fp32, each wave's acc scaled to the common max
+    float *const mo = (float *)ring;  // [W][g][HD] fp32, each stream's acc scaled to the common max
     {
         float M = -INFINITY;
 #pragma unroll
@@ -283,7 +322,7 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
             M = fmaxf(M, sm_m[w][c16]);
         const float cw = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
         if (c16 < g) {
-            float *dst = mo + ((size_t)wave * g + c16) * HD + 4 * r4;
+            float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 4 * r4;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 *(f32x4 *)(dst + 16 * dt) = acc[dt] * cw;
@@ -330,12 +369,16 @@ __global__ __launch_bounds__(W * 64) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// Launch shape per head_dim: waves per workgroup and LDS bytes per wave, measured on the
+// Launch shape per head_dim: page streams per workgroup and LDS bytes per wave, measured on the
 // decode workloads of both families. head_dim 512 (16 KB units): one wave with two units per
 // workgroup, four workgroups per CU, so a batch's (row, KV head, split) items mostly start
 // at once and no CU waits on a partly filled last round. head_dim 256 (8 KB units): two
-// waves with three units each, three workgroups per CU, which keeps the window-sized local
-// items (at most 1024 keys) from running one page at a time on few waves.
+// page streams of one wave with three units each, three workgroups per CU, which keeps the
+// window-sized local items (at most 1024 keys) from running one page at a time on few waves.
+// A head_dim 512 grid of at most one workgroup per CU (one long row, say) would leave each CU
+// one wave working through its pages one at a time, so there four waves share every page,
+// a quarter of the head dims each (with eight units of 4 KB in flight per wave). The score
+// partials are added in the same tree either way, so both shapes give the same bits.
 template <int HD>
 struct DecodeShape;
 template <>
@@ -346,13 +389,19 @@ template <>
 struct DecodeShape<256> {
     static constexpr int waves = 2, slice = 24 * 1024;
 };
+constexpr int kNumCUs = 256;
 
 template <int HD, bool SHARED>
 hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
     constexpr int W = DecodeShape<HD>::waves;
     constexpr int SLICE = DecodeShape<HD>::slice;
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, SLICE>, grid, dim3(W * 64), args, 0,
+    if constexpr (HD == 512) {
+        if ((int64_t)grid.x * grid.y * grid.z <= kNumCUs)
+            return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 1, 4, 32 * 1024>, grid,
+                                   dim3(4 * 64), args, 0, stream);
+    }
+    return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, 1, SLICE>, grid, dim3(W * 64), args, 0,
                            stream);
 }
 
