@@ -189,6 +189,37 @@ def local_decode_measure(torch, devio, workloads, traffic, stream, flush, steps=
             "mall_flushed_gbs": round(kv / tf / 1e9, 1)}
 
 
+def gemma12b_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
+    """The 12B geometry: global decode (batch 32, 16 q heads over one KV head, hd 512, contexts
+    ~U{1..8192}, split 512) as KV GB/s, and the 12B mixed step's prefill rows of both families as
+    TFLOP/s; every timed run after a MALL flush."""
+    b = workloads.cfg6_12b_global_decode()
+    s = b.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, b.ctx_lens)
+    d = devio.DeviceBatch(b)
+    for _ in range(10):
+        d.decode(512)
+    t = median(event_times(torch, stream, lambda: d.decode(512), steps, flush))
+    out = {"global_decode": {"workload": "12B global decode: batch 32, 16 q heads, 1 KV head, hd 512, contexts "
+                                         "~U{1..8192}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
+                             "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4)}}
+    del d
+    for fam in ("global", "local"):
+        pre, _ = workloads.cfg6_12b_mixed(fam)
+        dp = devio.DeviceBatch(pre)
+        s = pre.spec
+        flops = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens, pre.q_lens)
+        for _ in range(10):
+            dp.prefill()
+        tp = median(event_times(torch, stream, dp.prefill, 10, flush))
+        out[f"{fam}_prefill"] = {"workload": f"12B {fam} prefill: 4 chunks x 2048 queries, priors "
+                                             f"{pre.ctx_lens.tolist()}", "flops": flops, "ms": round(tp * 1e3, 4),
+                                 "tflops": round(flops / tp / 1e12, 2),
+                                 "frac_of_bf16_peak": round(flops / tp / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del dp
+    return out
+
+
 def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
     """The 60-layer decode sweep (5 local : 1 global, last global; 16 rows at 32768 tokens; global
     layers K=V with 1024-token splits, local layers 512) with every layer's pools resident, timed
@@ -232,6 +263,25 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
                        "heads, K=V, split 1024; local: hd 256, 16 KV heads, window 1024, split 512",
            "kv_bytes": kv_total, "ms": round(t * 1e3, 4), "gbs": round(kv_total / t / 1e9, 1),
            "frac": round(kv_total / t / 1e9 / HBM_PEAK_GBS, 4)}
+    # the same 60 calls captured once in a HIP graph and replayed (no launch gaps between layers)
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sweep()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            sweep()
+        graph.replay()
+        torch.cuda.synchronize()
+        tg = median(event_times(torch, stream, graph.replay, reps))
+        out["graph_ms"] = round(tg * 1e3, 4)
+        out["graph_gbs"] = round(kv_total / tg / 1e9, 1)
+        del graph
+    except Exception as e:  # report, never hide
+        out["graph_error"] = str(e)[:200]
     for fam in ("local", "global"):
         out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
         out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
@@ -362,6 +412,10 @@ def main():
             result["sweep"], result["long_decode"] = sweep_measure(torch, devio, workloads, traffic, stream, flush)
         except Exception as e:  # report, never hide
             result["sweep"] = {"error": str(e)[:300]}
+        try:
+            result["gemma12b"] = gemma12b_measure(torch, devio, workloads, traffic, stream, flush)
+        except Exception as e:  # report, never hide
+            result["gemma12b"] = {"error": str(e)[:300]}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(batch, kv_bytes)
     print(json.dumps(result), flush=True)

@@ -377,8 +377,10 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
 // window-sized local items (at most 1024 keys) from running one page at a time on few waves.
 // A head_dim 512 grid of at most one workgroup per CU (one long row, say) would leave each CU
 // one wave working through its pages one at a time, so there four waves share every page,
-// a quarter of the head dims each (with eight units of 4 KB in flight per wave). The score
-// partials are added in the same tree either way, so both shapes give the same bits.
+// a quarter of the head dims each (with eight units of 4 KB in flight per wave); up to two
+// workgroups per CU (a batch of a single-KV-head family, say) the same with four units per wave,
+// so that two workgroups fit a CU's LDS. The score partials are added in the same tree in every
+// shape, so all of them give the same bits.
 template <int HD>
 struct DecodeShape;
 template <>
@@ -397,8 +399,12 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
     constexpr int SLICE = DecodeShape<HD>::slice;
     void *args[] = {(void *)&a};
     if constexpr (HD == 512) {
-        if ((int64_t)grid.x * grid.y * grid.z <= kNumCUs)
+        const int64_t items = (int64_t)grid.x * grid.y * grid.z;
+        if (items <= kNumCUs)
             return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 1, 4, 32 * 1024>, grid,
+                                   dim3(4 * 64), args, 0, stream);
+        if (items <= 2 * kNumCUs)
+            return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 1, 4, 16 * 1024>, grid,
                                    dim3(4 * 64), args, 0, stream);
     }
     return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, 1, SLICE>, grid, dim3(W * 64), args, 0,

@@ -161,14 +161,15 @@ def test_bitwise_batch_invariance_and_reorder(devio):
 @pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "global-kv-shared"])
 def test_bitwise_dims_split_invariance(devio, spec):
     """A head_dim 512 grid of at most 256 (row, KV head, split) items runs four waves per item,
-    each on a quarter of the head dims; a larger grid runs one wave per item. A row gives the
-    same bits either way: alone, in 2- and 4-row batches (16 x 4 x 4 = 256 items at most) and
-    inside a 6-row batch (384 items). The small-grid results also match the oracle."""
-    L = workloads.ragged((14, int(spec.kv_shared)), 1, 8192, 6)
+    each on a quarter of the head dims, with 32 KB of LDS each; up to 512 items the same with
+    16 KB each; a larger grid runs one wave per item. A row gives the same bits in every shape:
+    alone, in 2- and 4-row batches (16 x 4 x 4 = 256 items at most), in a 6-row batch (384 items)
+    and inside a 10-row batch (640 items). The small-grid results also match the oracle."""
+    L = workloads.ragged((14, int(spec.kv_shared)), 1, 8192, 10)
     L[0], L[1], L[2] = 8192, 1, 513
-    b = workloads.make_batch(spec, L, np.ones(6, np.int32), (14, int(spec.kv_shared)), back="all")
+    b = workloads.make_batch(spec, L, np.ones(10, np.int32), (14, int(spec.kv_shared)), back="all")
     o_all, l_all = _run(devio, b, 512, max_ctx=8192)
-    for rows in ([0], [2, 5], [1, 3, 4, 0]):
+    for rows in ([0], [2, 5], [1, 3, 4, 0], [9, 8, 7, 6, 5, 4]):
         sub = b.subset(rows)
         o, l = _run(devio, sub, 512, max_ctx=8192)
         assert np.array_equal(o, o_all[rows]) and np.array_equal(l, l_all[rows]), rows

@@ -113,6 +113,11 @@ class LayerSpec:
 LOCAL_31B = LayerSpec("local", 32, 16, 256, window=1024)
 GLOBAL_31B = LayerSpec("global", 32, 4, 512)
 GLOBAL_31B_KV_SHARED = LayerSpec("global", 32, 4, 512, kv_shared=True)
+# The 12B line: its global family keeps a single KV head (the Core AI card's 12B control, "1 global
+# KV head"), here for 16 query heads (g = 16); its local family is read as 16 query heads over 8 KV
+# heads. Both are readings: the pages give no full 12B head table.
+LOCAL_12B = LayerSpec("local", 16, 8, 256, window=1024)
+GLOBAL_12B = LayerSpec("global", 16, 1, 512)
 
 
 # --------------------------------------------------------------------------- batches
@@ -291,18 +296,37 @@ def cfg3_local_decode(B: int = 64, lo: int = 512, hi: int = 32768, **kw) -> Batc
     return make_batch(LOCAL_31B, L, np.ones(B, np.int32), (3, 0), back="visible", **kw)
 
 
+def _mixed(spec: LayerSpec, cfg: int, fam: int, n_prefill: int, chunk: int, max_prior: int, n_decode: int,
+           max_decode_len: int, **kw):
+    prior = generator(cfg, fam, T_PRIOR).integers(0, max_prior + 1, size=n_prefill).astype(np.int32)
+    pre = make_batch(spec, prior + chunk, np.full(n_prefill, chunk, np.int32), (cfg, fam, 0),
+                     back="visible", **kw)
+    L = ragged((cfg, fam, 1), 1, max_decode_len, n_decode)
+    dec = make_batch(spec, L, np.ones(n_decode, np.int32), (cfg, fam, 1), back="visible", **kw)
+    return pre, dec
+
+
 def cfg4_mixed(family: str, n_prefill: int = 4, chunk: int = 2048, max_prior: int = 6144,
                n_decode: int = 60, max_decode_len: int = 8192, **kw):
     """Mixed step: prefill rows (chunk queries after a prior ~ U{0..max_prior}) and decode rows
     (L ~ U{1..max_decode_len}) of one family. Returns (prefill_batch, decode_batch)."""
     spec = GLOBAL_31B if family == "global" else LOCAL_31B
     fam = 1 if family == "global" else 0
-    prior = generator(4, fam, T_PRIOR).integers(0, max_prior + 1, size=n_prefill).astype(np.int32)
-    pre = make_batch(spec, prior + chunk, np.full(n_prefill, chunk, np.int32), (4, fam, 0),
-                     back="visible", **kw)
-    L = ragged((4, fam, 1), 1, max_decode_len, n_decode)
-    dec = make_batch(spec, L, np.ones(n_decode, np.int32), (4, fam, 1), back="visible", **kw)
-    return pre, dec
+    return _mixed(spec, 4, fam, n_prefill, chunk, max_prior, n_decode, max_decode_len, **kw)
+
+
+def cfg6_12b_global_decode(B: int = 32, max_len: int = 8192, **kw) -> Batch:
+    """12B global decode: B rows, 16 q heads, one KV head, hd 512, L ~ U{1..max_len}; split 512."""
+    L = ragged((6, 0), 1, max_len, B)
+    return make_batch(GLOBAL_12B, L, np.ones(B, np.int32), (6, 0), back="all", **kw)
+
+
+def cfg6_12b_mixed(family: str, n_prefill: int = 4, chunk: int = 2048, max_prior: int = 6144,
+                   n_decode: int = 60, max_decode_len: int = 8192, **kw):
+    """The mixed step at the 12B geometry (same row recipe as the 31B mixed step)."""
+    spec = GLOBAL_12B if family == "global" else LOCAL_12B
+    fam = 1 if family == "global" else 0
+    return _mixed(spec, 6, fam, n_prefill, chunk, max_prior, n_decode, max_decode_len, **kw)
 
 
 def cfg5_layer_spec(family: str) -> LayerSpec:
