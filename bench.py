@@ -149,6 +149,41 @@ def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
     return out
 
 
+def append_measure(torch, devio, workloads, stream, flush, iters=20):
+    """gattn_kv_append of the mixed step's new tokens (the 4 x 2048 prefill chunks and the 60 decode
+    tokens) for each 31B family: GB/s of algorithmic bytes, every new K (and V) element read once
+    and written once; each timed run after a MALL flush."""
+    import numpy as np
+    out = {}
+    for fam in ("global", "local"):
+        pre, dec = workloads.cfg4_mixed(fam)
+        s = pre.spec
+        rows = []
+        for b in (pre, dec):
+            d = devio.DeviceBatch(b)
+            n_new = b.q_lens.astype(np.int32)
+            cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+            T = int(cu[-1])
+            kn = torch.randn(T, s.num_kv_heads, s.head_dim, device="cuda").to(torch.bfloat16).view(torch.int16)
+            vn = torch.randn_like(kn, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+            rows.append((d, devio.dev(cu), kn, vn, b.B, int(n_new.max())))
+        nbytes = sum(kn.numel() * 2 * 2 * 2 for _, _, kn, _, _, _ in rows)  # K and V, read and written
+
+        def call():
+            for d, cu, kn, vn, B, mx in rows:
+                devio.nat.gattn_kv_append(d.layer, kn, vn, d.k_pool, d.v_pool, d.num_pages, d.page_table,
+                                          d.pt_stride, cu, d.ctx_lens, B, mx, None)
+        for _ in range(5):
+            call()
+        t = median(event_times(torch, stream, call, iters, flush))
+        out[fam] = {"tokens": int(sum(kn.shape[0] for _, _, kn, _, _, _ in rows)), "bytes": nbytes,
+                    "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1)}
+        del rows
+    out["workload"] = ("gattn_kv_append of the mixed step's 8252 new tokens per family (4 prefill chunks of 2048, "
+                       "60 decode tokens) into the 31B pools, two calls")
+    return out
+
+
 def event_times(torch, stream, fn, n, flush=None):
     """Per-call durations (s) of ``fn`` from HIP events recorded on ``stream``; with ``flush``, a
     1 GiB buffer is overwritten before each call, outside the events."""
@@ -406,6 +441,10 @@ def main():
             result["prefill"] = prefill_measure(torch, devio, workloads, traffic, flush)
         except Exception as e:  # report, never hide
             result["prefill"] = {"error": str(e)[:200]}
+    try:
+        result["kv_append"] = append_measure(torch, devio, workloads, stream, flush)
+    except Exception as e:  # report, never hide
+        result["kv_append"] = {"error": str(e)[:200]}
     if not args.no_sweep:
         try:
             result["local_decode"] = local_decode_measure(torch, devio, workloads, traffic, stream, flush)

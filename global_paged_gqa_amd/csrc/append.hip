@@ -1,0 +1,86 @@
+// KV append on gfx950: the K and V rows of new tokens copied into their pages.
+//
+// Row r appends n = cu_new[r+1] - cu_new[r] tokens at positions ctx_lens[r] - n + i; token t
+// lands in page page_table[r][t / 16], slot t % 16, and its (kv_head) row of head_dim bf16 is
+// contiguous in both the source and the (page, kv_head) block of the pool (the paged layout of
+// the gattn.h header; the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan's checked page offsets).
+// One workgroup copies kTok tokens of one row: each lane owns one 16-byte chunk position of a
+// (token, kv_head) row and steps through rows, kUnroll of them loaded before any is stored, so
+// every wave reads and writes whole contiguous rows with several loads in flight, and a row's
+// page id is looked up once per row. It is a pure copy, bound by HBM bandwidth: 2 * head_dim * 2 bytes read and
+// written per (token, kv_head) and pool (K, and V unless V is the K cache).
+#include "common.h"
+#include "kernels.h"
+
+namespace gattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = 4;     // tokens per workgroup
+constexpr int kUnroll = 4;  // rows a lane loads before it stores them (loads in flight)
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
+    constexpr int CPR = HD / 8;           // 16-byte chunks per (token, kv_head) row
+    constexpr int RPI = kThreads / CPR;   // rows a workgroup copies per step
+    const int r = blockIdx.y;
+    const int n0 = a.cu_new[r], n = a.cu_new[r + 1] - n0;
+    const int i0 = blockIdx.x * kTok;
+    if (i0 >= n)
+        return;
+    const int L = a.ctx_lens[r];
+    const int nt = min(kTok, n - i0);
+    const int Hkv = a.num_kv_heads;
+    const int rows = nt * Hkv;
+    const int32_t *pt = a.page_table + (int64_t)r * a.pt_stride;
+    const int c = threadIdx.x % CPR, sub = threadIdx.x / CPR;  // this lane's chunk of its rows
+    int bad = 0;
+    for (int row0 = sub; row0 < rows; row0 += RPI * kUnroll) {
+        u32x4 kv[kUnroll], vv[kUnroll];
+        int64_t dst[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = row0 + u * RPI;
+            dst[u] = -1;
+            if (row >= rows)
+                continue;
+            const int it = row / Hkv, kvh = row - it * Hkv;
+            const int t = L - n + i0 + it;  // absolute position of the token
+            const int pid = (L >= n && (t >> 4) < a.pt_stride) ? pt[t >> 4] : -1;
+            if (pid < 0 || pid >= a.num_pages) {
+                bad = 1;
+                continue;
+            }
+            const int64_t src = ((int64_t)(n0 + i0 + it) * Hkv + kvh) * HD + c * 8;
+            dst[u] = (((int64_t)pid * Hkv + kvh) * kPage + (t & (kPage - 1))) * HD + c * 8;
+            kv[u] = *(const u32x4 *)(a.k_new + src);
+            if (a.v_new)
+                vv[u] = *(const u32x4 *)(a.v_new + src);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (dst[u] < 0)
+                continue;
+            *(u32x4 *)(a.k_pool + dst[u]) = kv[u];
+            if (a.v_new)
+                *(u32x4 *)(a.v_pool + dst[u]) = vv[u];
+        }
+    }
+    if (a.status && __builtin_amdgcn_ballot_w64(bad) && (threadIdx.x & 63) == 0)
+        atomicOr(a.status, 1);
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, hipStream_t stream) {
+    const dim3 grid((a.max_new + kTok - 1) / kTok, batch);
+    void *args[] = {(void *)&a};
+    if (head_dim == 256)
+        return hipLaunchKernel((const void *)kv_append_kernel<256>, grid, dim3(kThreads), args, 0, stream);
+    if (head_dim == 512)
+        return hipLaunchKernel((const void *)kv_append_kernel<512>, grid, dim3(kThreads), args, 0, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gattn

@@ -230,6 +230,44 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
     return GATTN_OK;
 }
 
+int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                    uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                    const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
+                    void *stream) {
+    int rc = check_layer(layer);
+    if (rc != GATTN_OK)
+        return rc;
+    if (batch < 0 || max_new < 0 || pt_stride < 1 || num_pages < 1)
+        return GATTN_ERR_BAD_SHAPE;
+    if (!k_new || !k_pool || !page_table || !cu_new || !ctx_lens)
+        return GATTN_ERR_NULL_PTR;
+    if (layer->kv_shared) {
+        if (v_new || (v_pool && v_pool != k_pool))
+            return GATTN_ERR_BAD_SHAPE;
+        v_pool = nullptr;
+    } else if (!v_new || !v_pool) {
+        return GATTN_ERR_NULL_PTR;
+    }
+    if (batch == 0 || max_new == 0)
+        return GATTN_OK;
+    gattn::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = layer->kv_shared ? nullptr : v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.page_table = page_table;
+    a.cu_new = cu_new;
+    a.ctx_lens = ctx_lens;
+    a.status = status;
+    a.num_pages = num_pages;
+    a.pt_stride = pt_stride;
+    a.num_kv_heads = layer->num_kv_heads;
+    a.max_new = max_new;
+    if (gattn::launch_kv_append(a, layer->head_dim, batch, (hipStream_t)stream) != hipSuccess)
+        return GATTN_ERR_HIP;
+    return GATTN_OK;
+}
+
 int gattn_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
                   const float *lse_part, uint16_t *out, float *lse, void *stream) {
     if (batch < 0 || num_q_heads <= 0 || num_splits <= 0 || head_dim <= 0)

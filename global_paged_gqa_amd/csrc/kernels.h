@@ -43,6 +43,23 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+struct AppendArgs {
+    const uint16_t *k_new;
+    const uint16_t *v_new;   // null: only K is written (V is the K cache)
+    uint16_t *k_pool;
+    uint16_t *v_pool;
+    const int32_t *page_table;
+    const int32_t *cu_new;
+    const int32_t *ctx_lens;
+    int32_t *status;         // may be null
+    int64_t num_pages;
+    int pt_stride;
+    int num_kv_heads;
+    int max_new;
+};
+
+hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, hipStream_t stream);
+
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                hipStream_t stream);
 

@@ -193,6 +193,37 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
 int gattn_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
                   const float *lse_part, uint16_t *out, float *lse, void *stream);
 
+/*
+ * KV append: write the K and V rows of newly computed tokens into their pages,
+ * the step just before attention (a decode step adds one token per row, a
+ * prefill chunk adds the chunk; the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan
+ * routes these page writes through the same checked offsets as the reads). Row
+ * r appends n_r = cu_new[r+1] - cu_new[r] tokens at absolute positions
+ * ctx_lens[r] - n_r + i, i in [0, n_r): ctx_lens counts the cache after the
+ * append, exactly as gattn_decode and gattn_prefill then read it. Token t of
+ * row r goes to page page_table[r * pt_stride + t / 16], slot t % 16 (layout
+ * above). Only those slots are written; every other pool byte keeps its value.
+ *
+ *   k_new      [total_new][num_kv_heads][head_dim] bf16, rows back to back in
+ *              cu_new order.
+ *   v_new      same shape, or NULL when layer->kv_shared (V is the K cache).
+ *   k_pool     written; v_pool written, or NULL / equal to k_pool when kv_shared.
+ *   num_pages  pages in each pool.
+ *   page_table [batch][pt_stride] int32 (device memory).
+ *   cu_new     [batch + 1] int32 (device memory), cu_new[0] = 0, nondecreasing.
+ *   ctx_lens   [batch] int32 (device memory), ctx_lens[r] >= n_r.
+ *   max_new    host-side upper bound of every n_r (sets the grid).
+ *   status     optional int32 (device memory, may be NULL). Fail closed: a token
+ *              whose position lies beyond the page table, whose page id is
+ *              outside [0, num_pages), or whose row has ctx_lens[r] < n_r is not
+ *              written, and the kernel ORs 1 into *status. The caller clears it.
+ * Rows with n_r = 0 are skipped. Enqueues one kernel on `stream`.
+ */
+int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                    uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                    const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,9 @@ def _load():
             lib.oracle_layer_is_global.argtypes = [c_int, c_int]
             lib.oracle_threads.restype = c_int
             lib.oracle_threads.argtypes = []
+            lib.oracle_kv_append.restype = ctypes.c_int64
+            lib.oracle_kv_append.argtypes = [c_int, c_int, c_int, c_int, i32p, i32p, i32p, c_int, ctypes.c_int64,
+                                             u16p, u16p, u16p, u16p]
             _lib = lib
     return _lib
 
@@ -135,6 +138,27 @@ def merge(lse_parts, o_parts):
     if rc != OK:
         raise OracleError(f"oracle_merge failed: {rc}")
     return out, lse
+
+
+def kv_append(num_kv_heads: int, head_dim: int, page_size: int, cu_new, ctx_lens, page_table, num_pages: int,
+              k_new, v_new, k_pool, v_pool):
+    """Paged KV append (``oracle_kv_append``): returns (k_pool', v_pool', skipped tokens) with the
+    new tokens copied into copies of the given pools."""
+    lib = _load()
+    cu_new, ctx_lens = _i32(cu_new), _i32(ctx_lens)
+    pt = _i32(page_table)
+    k_new = _u16(k_new)
+    v_new = None if v_new is None else _u16(v_new)
+    kp = np.array(k_pool, dtype=np.uint16, copy=True, order="C")
+    vp = None if v_pool is None else np.array(v_pool, dtype=np.uint16, copy=True, order="C")
+    B = int(ctx_lens.shape[0])
+    n = lib.oracle_kv_append(num_kv_heads, head_dim, page_size, B, _ptr(cu_new, ctypes.c_int32),
+                             _ptr(ctx_lens, ctypes.c_int32), _ptr(pt, ctypes.c_int32), int(pt.shape[1]),
+                             int(num_pages), _ptr(k_new, ctypes.c_uint16), _ptr(v_new, ctypes.c_uint16),
+                             _ptr(kp, ctypes.c_uint16), _ptr(vp, ctypes.c_uint16))
+    if n < 0:
+        raise OracleError(f"oracle_kv_append failed: {n}")
+    return kp, vp, int(n)
 
 
 def layer_is_global(layer: int, n_layers: int) -> int:

@@ -26,6 +26,11 @@
  * K and V are contiguous per row (no pages): row r stores tokens
  * [k_start[r], ctx_len[r]) back to back as [token][kv_head][head_dim].
  *
+ * The KV append writes new tokens into the paged cache by the layout's own definition (token t
+ * of a row in page page_table[row][t / page_size], slot t % page_size, pool laid out
+ * [page][kv_head][slot][head_dim]; the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan asks that page
+ * offsets come from one checked place), element by element, with no blocking.
+ *
  * The split-KV routine follows the pegainfer "[Model] Gemma 4 M3 31B" plan's
  * split-KV chunk policy in its plainest reading: cut a row's keys at absolute
  * multiples of the split size, attend each piece on its own, then merge the
@@ -333,4 +338,45 @@ int oracle_threads(void)
 #else
     return 1;
 #endif
+}
+
+int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool)
+{
+    if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
+        !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool))
+        return ORACLE_BAD_ARG;
+    int64_t skipped = 0;
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = (int64_t)cu_new[r + 1] - cu_new[r];
+        if ((int64_t)ctx_lens[r] < n) { /* more new tokens than the cache holds: the row is malformed */
+            skipped += n;
+            continue;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t t = (int64_t)ctx_lens[r] - n + i; /* absolute position of the new token */
+            const int64_t logical = t < 0 ? -1 : t / page_size;
+            if (t < 0 || logical >= pt_stride) {
+                ++skipped;
+                continue;
+            }
+            const int64_t page = page_table[(int64_t)r * pt_stride + logical];
+            if (page < 0 || page >= num_pages) {
+                ++skipped;
+                continue;
+            }
+            const int64_t slot = t % page_size;
+            const int64_t src_tok = (int64_t)cu_new[r] + i;
+            for (int kv = 0; kv < Hkv; ++kv)
+                for (int d = 0; d < hd; ++d) {
+                    const int64_t dst = ((page * Hkv + kv) * page_size + slot) * hd + d;
+                    const int64_t src = (src_tok * Hkv + kv) * hd + d;
+                    k_pool[dst] = k_new[src];
+                    if (v_new)
+                        v_pool[dst] = v_new[src];
+                }
+        }
+    }
+    return skipped;
 }

@@ -45,6 +45,17 @@ int oracle_merge(int64_t n_rows, int n_parts, int hd, const double *lse_parts, c
  * five-local-one-global groups (the stack must end on a global layer). */
 int oracle_layer_is_global(int layer, int n_layers);
 
+/* KV append, the plain definition of the paged layout: row r's n_r = cu_new[r+1] - cu_new[r] new
+ * tokens sit at positions t = ctx_lens[r] - n_r + i; token t of row r is stored in page
+ * page_table[r][t / page_size], slot t % page_size, as pool[page][kv_head][slot][head_dim]. For
+ * every such token whose position fits the table and whose page id is in [0, num_pages), copies
+ * its [Hkv][hd] K row (and V row when v_new is not NULL) into the pools; all other pool values
+ * stay. A row with ctx_lens[r] < n_r is malformed and writes nothing. Returns the number of tokens
+ * skipped (malformed row, position beyond the table, page id out of range), or ORACLE_BAD_ARG. */
+int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool);
+
 /* OpenMP threads the oracle runs with. */
 int oracle_threads(void);
 

@@ -27,7 +27,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
-                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine"])
+                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine",
+                            "gattn_kv_append"])
     for n in names:
         assert hasattr(nat._lib, n), n
     assert g.gattn_abi_version() == 1
@@ -162,6 +163,32 @@ def test_prefill_and_combine_reject_bad_arguments():
     assert st(g.gattn_combine, 4, 32, 510, 3, 1, 2, 3, 4) == nat.ERR_UNSUPPORTED
     assert st(g.gattn_combine, 4, 32, 512, 3, None, 2, 3, 4) == nat.ERR_NULL_PTR
     assert st(g.gattn_combine, 0, 32, 512, 3, 1, 2, 3, 4) == 0
+
+
+def test_kv_append_rejects_bad_arguments():
+    lay = g.make_layer("global", 32, 4, 512)
+    ok = dict(k_new=1, v_new=2, k_pool=3, v_pool=4, num_pages=10, page_table=5, pt_stride=8, cu_new=6, ctx_lens=7,
+              batch=0, max_new=16, status=None)
+
+    def st(layer, **kw):
+        try:
+            g.gattn_kv_append(layer, **kw, stream=0)
+        except g.GattnError as e:
+            return e.status
+        return 0
+    assert st(lay, **ok) == 0
+    for key in ("k_new", "v_new", "k_pool", "v_pool", "page_table", "cu_new", "ctx_lens"):
+        assert st(lay, **dict(ok, **{key: None})) == nat.ERR_NULL_PTR, key
+    assert st(lay, **dict(ok, batch=-1)) == nat.ERR_BAD_SHAPE
+    assert st(lay, **dict(ok, max_new=-1)) == nat.ERR_BAD_SHAPE
+    assert st(lay, **dict(ok, pt_stride=0)) == nat.ERR_BAD_SHAPE
+    assert st(lay, **dict(ok, num_pages=0)) == nat.ERR_BAD_SHAPE
+    assert st(g.make_layer("global", 32, 4, 128), **ok) == nat.ERR_UNSUPPORTED
+    shared = g.make_layer("global", 32, 4, 512, kv_shared=True)
+    assert st(shared, **dict(ok, v_new=None, v_pool=None)) == 0
+    assert st(shared, **dict(ok, v_new=None, v_pool=3)) == 0          # v_pool == k_pool
+    assert st(shared, **dict(ok, v_new=2, v_pool=None)) == nat.ERR_BAD_SHAPE
+    assert st(shared, **dict(ok, v_new=None, v_pool=4)) == nat.ERR_BAD_SHAPE
 
 
 def test_one_hip_runtime_in_process():

@@ -332,3 +332,76 @@ def test_brute_force_distinguishes_interleaved_mapping():
     bo, _ = brute_attend(True, Hq, Hkv, hd, 0, 0.5, L, list(range(L)), as_floats(q), as_floats(k),
                          as_floats(v), kv_of=lambda h, Hq, Hkv: h % Hkv)
     assert np.max(np.abs(out - np.array(bo, float))) > 1e-3
+
+
+# ------------------------------------------------------------------------ KV append
+def _append_case(spec, ctx_lens, n_new, key):
+    """A batch whose pool holds every token, the pool with the last n_new tokens of each row
+    cleared, and those tokens' K/V rows gathered from the contiguous side."""
+    b = workloads.make_batch(spec, ctx_lens, np.ones(len(ctx_lens), np.int32), key, back="all")
+    n_new = np.asarray(n_new, np.int32)
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    k_new, v_new = [], []
+    for r in range(b.B):
+        kk, vv = b.row_keys(r)
+        n = int(n_new[r])
+        k_new.append(kk[len(kk) - n:])
+        v_new.append(vv[len(vv) - n:])
+    k_new = np.concatenate(k_new)
+    v_new = None if spec.kv_shared else np.concatenate(v_new)
+    return b, cu, k_new, v_new
+
+
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.LOCAL_31B, workloads.GLOBAL_31B_KV_SHARED],
+                         ids=["global", "local", "kv-shared"])
+def test_kv_append_rebuilds_the_scattered_pool(spec):
+    """Appending each row's last n tokens into a pool where their slots were zeroed gives back the
+    pool that workloads' own scatter built (n crossing page edges, 0-token rows included), and no
+    other byte changes; every written slot is where the library's checked helper places it."""
+    L = [1, 17, 40, 300, 513, 1024]
+    n_new = [1, 2, 0, 45, 16, 300]
+    b, cu, k_new, v_new = _append_case(spec, L, n_new, (40, spec.num_kv_heads, int(spec.kv_shared)))
+    P = spec.page_size
+    kp0, vp0 = b.k_pool.copy(), None if b.v_pool is None else b.v_pool.copy()
+    # clear the appended tokens' slots by walking the table directly (independent of the oracle)
+    for r in range(b.B):
+        for t in range(L[r] - n_new[r], L[r]):
+            kp0[b.page_table[r, t // P], :, t % P, :] = 0
+            if vp0 is not None:
+                vp0[b.page_table[r, t // P], :, t % P, :] = 0
+    kp, vp, skipped = oracle.kv_append(spec.num_kv_heads, spec.head_dim, P, cu, L, b.page_table, b.num_pages,
+                                       k_new, v_new, kp0, vp0)
+    assert skipped == 0
+    assert np.array_equal(kp, b.k_pool)
+    if vp is not None:
+        assert np.array_equal(vp, b.v_pool)
+    import global_paged_gqa_amd as g
+    lay = g.make_layer(spec.family, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.window,
+                       spec.kv_shared)
+    flat = kp.reshape(-1)
+    for r, t, kvh in ((3, L[3] - 45, 0), (3, L[3] - 1, spec.num_kv_heads - 1), (5, 724, 1), (1, 16, 0)):
+        off = g.gattn_kv_offset(lay, b.page_table, b.B, b.pt_stride, r, t, kvh, b.num_pages)
+        i = int(cu[r]) + t - (L[r] - n_new[r])
+        assert np.array_equal(flat[off:off + spec.head_dim], k_new[i, kvh]), (r, t)
+
+
+def test_kv_append_fails_closed():
+    """A token whose page id is out of range or -1, or whose position is beyond the table, is
+    skipped and counted; a row with fewer cached tokens than new ones writes none of them; the
+    rest are written."""
+    Hkv, hd, P = 2, 8, 16
+    pt = np.array([[2, -1, 9], [0, 1, 2]], np.int32)       # row 0: page 1 unbacked, page 2 = id 9 >= 4
+    kp = np.zeros((4, Hkv, P, hd), np.uint16)
+    L = np.array([40, 3], np.int32)
+    n_new = np.array([30, 5], np.int32)                    # row 0: tokens 10..39; row 1: 5 > L
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    k_new = (np.arange(int(cu[-1]) * Hkv * hd, dtype=np.int64) % 60000 + 1).astype(np.uint16).reshape(-1, Hkv, hd)
+    kp2, _, skipped = oracle.kv_append(Hkv, hd, P, cu, L, pt, 4, k_new, None, kp, None)
+    # row 0: tokens 10..15 in page 2 (written); 16..31 page -1 (skipped); 32..39 page 9 (skipped)
+    # row 1: 5 new tokens but 3 cached: none written
+    assert skipped == 16 + 8 + 5
+    assert np.array_equal(kp2[2, :, 10:16], np.transpose(k_new[0:6], (1, 0, 2)))
+    untouched = np.ones(kp.shape, bool)
+    untouched[2, :, 10:16] = False
+    assert np.all(kp2[untouched] == 0)
+
