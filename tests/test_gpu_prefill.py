@@ -157,6 +157,42 @@ def test_window_counts_multi_window_chunk(devio):
     assert np.array_equal(np.round(np.exp(lse)).astype(np.int64), np.repeat(n[:, None], 4, 1))
 
 
+@pytest.mark.parametrize("spec", [workloads.LayerSpec("local", 4, 2, 256, window=1024, scale=1.0),
+                                  workloads.LayerSpec("global", 16, 2, 512, scale=1.0)], ids=["local", "global"])
+def test_prefill_position_probe(devio, spec):
+    """One key dominates: every query is e_0 and K[t*] = 200 e_0 (all other keys 0), so for a query
+    that sees t* every other weight underflows to exactly 0 and O must equal V[t*] bit for bit; a
+    query that cannot see t* (before it, or past the window) gets the uniform mean of the others.
+    t* sweeps page, 32-key block, query-tile and window edges of a 1300-query chunk after 200
+    cached tokens."""
+    prior, C = 200, 1300
+    L = prior + C
+    for t_star in (0, 15, 16, 31, 32, 199, 200, 201, 263, 264, 700, 1023, 1024, L - 1):
+        b = workloads.make_batch(spec, [L], [C], (35, t_star), back="all")
+        P = spec.page_size
+        b.q[:] = 0
+        b.q[:, :, 0] = workloads.f32_to_bf16_bits(np.float32([1.0]))[0]
+        kk = np.zeros_like(b.k)
+        kk[t_star, :, 0] = workloads.f32_to_bf16_bits(np.float32([200.0]))[0]
+        code = workloads.f32_to_bf16_bits(np.float32(np.arange(spec.head_dim) + 0.5 + (t_star % 97)))
+        vv = b.v.copy()
+        vv[t_star] = code
+        for t in range(L):
+            b.k_pool[b.page_table[0, t // P], :, t % P, :] = kk[t]
+            b.v_pool[b.page_table[0, t // P], :, t % P, :] = vv[t]
+        b.k[:] = kk
+        b.v[:] = vv
+        out, lse = devio.prefill(b)
+        want = workloads.bf16_bits_to_f32(code).astype(np.float64)
+        pos = prior + np.arange(C)
+        sees = (pos >= t_star) & ((pos - t_star < spec.window) if not spec.is_global else True)
+        assert sees.any(), t_star
+        for i in np.nonzero(sees)[0]:
+            for h in range(spec.num_q_heads):
+                assert np.array_equal(out[i, h], want), (t_star, i, h)
+        check(b, out, lse, tag=f"{spec.family} position probe t*={t_star}", bf16_slack=True)
+
+
 def test_prefill_bitwise_invariances(devio):
     spec = workloads.GLOBAL_31B
     b = workloads.make_batch(spec, [700, 300, 1500], [200, 300, 90], (34, 0), back="all")
