@@ -31,6 +31,18 @@
  * [page][kv_head][slot][head_dim]; the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan asks that page
  * offsets come from one checked place), element by element, with no blocking.
  *
+ * The FP8 KV pool (the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan's opt-in FP8 KV pool for the
+ * sliding family; the vLLM Gemma 4 recipe's "--kv-cache-dtype fp8") stores each K and V element as
+ * one byte in the OCP 8-bit floating-point format E4M3 (sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the all-ones exponent with
+ * all-ones mantissa is NaN; there are no infinities, so the largest finite magnitude is 448).
+ * The pages fix neither the format variant nor the scale granularity; the reading taken here is
+ * E4M3 with one scale per tensor: the stored element stands for code_value * k_scale (K) or
+ * code_value * v_scale (V). Attention over such a pool is the same definition as above with
+ * K and V replaced by those exact values. Writing into it rounds the fp32 quotient x / scale
+ * to the nearest E4M3 value, ties to the even code, saturating finite magnitudes above 448 to
+ * 448 and keeping NaN (another reading: the pages give no rounding rule).
+ *
  * The split-KV routine follows the pegainfer "[Model] Gemma 4 M3 31B" plan's
  * split-KV chunk policy in its plainest reading: cut a row's keys at absolute
  * multiples of the split size, attend each piece on its own, then merge the
@@ -53,6 +65,45 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
+/* Value of an E4M3 code, from the format's definition (sign, biased exponent, mantissa). */
+static double e4m3_value(uint8_t c)
+{
+    const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const double mag = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+double oracle_e4m3_value(uint8_t code) { return e4m3_value(code); }
+
+uint8_t oracle_e4m3_encode(float x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    if (isnan(x))
+        return sign | 0x7f;
+    const double a = fabs((double)x);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    /* nearest of the finite magnitudes (codes 0x00 .. 0x7e); on a tie the even code */
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7e; ++c) {
+        const double d = fabs(e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+void oracle_e4m3_encode_n(int64_t n, const float *x, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_encode(x[i]);
+}
+
 /* First key position visible to a query at position p. */
 static int64_t visible_lo(int is_global, int window, int64_t p)
 {
@@ -70,6 +121,9 @@ typedef struct {
     const uint16_t *q, *k, *v;
     int64_t *q_off;   /* [B+1] first query index of each row */
     int64_t *k_off;   /* [B]   first stored token index of each row */
+    int fp8;          /* K and V are E4M3 codes (k8, v8) standing for code_value * k_scale / v_scale */
+    const uint8_t *k8, *v8;
+    double k_scale, v_scale;
 } problem;
 
 static int check_and_index(problem *pb)
@@ -117,10 +171,11 @@ static int row_of_query(const problem *pb, int64_t t)
     return lo;
 }
 
-static const uint16_t *key_ptr(const problem *pb, const uint16_t *base, int r, int64_t j, int kv)
+/* Element offset of token j's row (KV head kv) of row r in the contiguous K / V arrays. */
+static int64_t key_index(const problem *pb, int r, int64_t j, int kv)
 {
     int64_t k0 = pb->k_starts ? pb->k_starts[r] : 0;
-    return base + ((pb->k_off[r] + (j - k0)) * pb->Hkv + kv) * (int64_t)pb->hd;
+    return ((pb->k_off[r] + (j - k0)) * pb->Hkv + kv) * (int64_t)pb->hd;
 }
 
 /* Attend keys [a, b] (inclusive) of row r for one query vector; two-pass softmax.
@@ -132,10 +187,16 @@ static double attend_range(const problem *pb, int r, int kv, const double *qv,
     int64_t n = b - a + 1;
     double m = -INFINITY;
     for (int64_t j = a; j <= b; ++j) {
-        const uint16_t *kr = key_ptr(pb, pb->k, r, j, kv);
         double dot = 0.0;
-        for (int d = 0; d < hd; ++d)
-            dot += qv[d] * widen_bf16(kr[d]);
+        if (pb->fp8) {
+            const uint8_t *kr = pb->k8 + key_index(pb, r, j, kv);
+            for (int d = 0; d < hd; ++d)
+                dot += qv[d] * (e4m3_value(kr[d]) * pb->k_scale);
+        } else {
+            const uint16_t *kr = pb->k + key_index(pb, r, j, kv);
+            for (int d = 0; d < hd; ++d)
+                dot += qv[d] * widen_bf16(kr[d]);
+        }
         double s = pb->scale * dot;
         scores[j - a] = s;
         if (s > m)
@@ -149,20 +210,26 @@ static double attend_range(const problem *pb, int r, int kv, const double *qv,
         o[d] = 0.0;
     for (int64_t j = a; j <= b; ++j) {
         double w = exp(scores[j - a] - lse);
-        const uint16_t *vr = key_ptr(pb, pb->v, r, j, kv);
-        for (int d = 0; d < hd; ++d)
-            o[d] += w * widen_bf16(vr[d]);
+        if (pb->fp8) {
+            const uint8_t *vr = pb->v8 + key_index(pb, r, j, kv);
+            for (int d = 0; d < hd; ++d)
+                o[d] += w * (e4m3_value(vr[d]) * pb->v_scale);
+        } else {
+            const uint16_t *vr = pb->v + key_index(pb, r, j, kv);
+            for (int d = 0; d < hd; ++d)
+                o[d] += w * widen_bf16(vr[d]);
+        }
     }
     return lse;
 }
 
-int oracle_attend(int is_global, int Hq, int Hkv, int hd, int window, double scale,
-                  int B, const int32_t *q_lens, const int32_t *ctx_lens, const int32_t *k_starts,
-                  const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  double *out, double *lse)
+/* Every (query, query head) of the problem, in parallel. */
+static int attend_problem(problem *pbp, double *out, double *lse)
 {
-    problem pb = {is_global, Hq, Hkv, hd, window, scale, B, q_lens, ctx_lens, k_starts,
-                  q, k, v ? v : k, NULL, NULL};
+    problem pb = *pbp;
+    const int is_global = pb.is_global, Hq = pb.Hq, Hkv = pb.Hkv, hd = pb.hd, window = pb.window, B = pb.B;
+    const int32_t *q_lens = pb.q_lens, *ctx_lens = pb.ctx_lens;
+    const uint16_t *q = pb.q;
     int rc = check_and_index(&pb);
     if (rc != ORACLE_OK) {
         free(pb.q_off);
@@ -207,6 +274,28 @@ int oracle_attend(int is_global, int Hq, int Hkv, int hd, int window, double sca
     free(pb.q_off);
     free(pb.k_off);
     return failed ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+int oracle_attend(int is_global, int Hq, int Hkv, int hd, int window, double scale,
+                  int B, const int32_t *q_lens, const int32_t *ctx_lens, const int32_t *k_starts,
+                  const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  double *out, double *lse)
+{
+    problem pb = {is_global, Hq, Hkv, hd, window, scale, B, q_lens, ctx_lens, k_starts,
+                  q, k, v ? v : k, NULL, NULL, 0, NULL, NULL, 1.0, 1.0};
+    return attend_problem(&pb, out, lse);
+}
+
+int oracle_attend_fp8kv(int is_global, int Hq, int Hkv, int hd, int window, double scale,
+                        int B, const int32_t *q_lens, const int32_t *ctx_lens, const int32_t *k_starts,
+                        const uint16_t *q, const uint8_t *k, const uint8_t *v, double k_scale, double v_scale,
+                        double *out, double *lse)
+{
+    if (!k || !v || !(k_scale > 0.0) || !(v_scale > 0.0) || isinf(k_scale) || isinf(v_scale))
+        return ORACLE_BAD_ARG;
+    problem pb = {is_global, Hq, Hkv, hd, window, scale, B, q_lens, ctx_lens, k_starts,
+                  q, NULL, NULL, NULL, NULL, 1, k, v, k_scale, v_scale};
+    return attend_problem(&pb, out, lse);
 }
 
 /* Merge pieces by logsumexp: M = max lse_i, LSE = M + ln sum_i exp(lse_i - M),
@@ -262,7 +351,7 @@ int oracle_decode_split(int is_global, int Hq, int Hkv, int hd, int window, doub
     for (int r = 0; r < B; ++r)
         ones[r] = 1;
     problem pb = {is_global, Hq, Hkv, hd, window, scale, B, ones, ctx_lens, k_starts,
-                  q, k, v ? v : k, NULL, NULL};
+                  q, k, v ? v : k, NULL, NULL, 0, NULL, NULL, 1.0, 1.0};
     int rc = check_and_index(&pb);
     if (rc != ORACLE_OK) {
         free(pb.q_off);
@@ -340,13 +429,19 @@ int oracle_threads(void)
 #endif
 }
 
-int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool)
+/* Destination of the new tokens: bf16 pools (k_pool, v_pool) or E4M3 pools (k_pool8, v_pool8) with
+ * their scales. */
+typedef struct {
+    uint16_t *k_pool, *v_pool;
+    uint8_t *k_pool8, *v_pool8;
+    float k_scale, v_scale;
+} append_dst;
+
+static int64_t append_rows(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                           const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                           const uint16_t *v_new, const append_dst *dst_pools)
 {
-    if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
-        !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool))
-        return ORACLE_BAD_ARG;
+    const int fp8 = dst_pools->k_pool8 != NULL;
     int64_t skipped = 0;
     for (int r = 0; r < B; ++r) {
         const int64_t n = (int64_t)cu_new[r + 1] - cu_new[r];
@@ -372,11 +467,42 @@ int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *c
                 for (int d = 0; d < hd; ++d) {
                     const int64_t dst = ((page * Hkv + kv) * page_size + slot) * hd + d;
                     const int64_t src = (src_tok * Hkv + kv) * hd + d;
-                    k_pool[dst] = k_new[src];
-                    if (v_new)
-                        v_pool[dst] = v_new[src];
+                    if (fp8) {
+                        /* the fp32 quotient, rounded to E4M3 */
+                        dst_pools->k_pool8[dst] = oracle_e4m3_encode((float)widen_bf16(k_new[src]) / dst_pools->k_scale);
+                        if (v_new)
+                            dst_pools->v_pool8[dst] =
+                                oracle_e4m3_encode((float)widen_bf16(v_new[src]) / dst_pools->v_scale);
+                    } else {
+                        dst_pools->k_pool[dst] = k_new[src];
+                        if (v_new)
+                            dst_pools->v_pool[dst] = v_new[src];
+                    }
                 }
         }
     }
     return skipped;
+}
+
+int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool)
+{
+    if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
+        !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool))
+        return ORACLE_BAD_ARG;
+    const append_dst d = {k_pool, v_pool, NULL, NULL, 1.0f, 1.0f};
+    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, k_new, v_new, &d);
+}
+
+int64_t oracle_kv_append_fp8(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                             const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                             const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool, uint8_t *v_pool)
+{
+    if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
+        !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool) || !(k_scale > 0.0f) ||
+        !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+        return ORACLE_BAD_ARG;
+    const append_dst d = {NULL, NULL, k_pool, v_pool, k_scale, v_scale};
+    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, k_new, v_new, &d);
 }

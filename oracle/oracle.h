@@ -56,6 +56,28 @@ int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *c
                          const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
                          const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool);
 
+/* FP8 KV pool: K and V hold OCP E4M3 codes (one byte per element, same [token][Hkv][hd] layout as
+ * above) standing for code_value * k_scale and code_value * v_scale (one scale per tensor, both
+ * positive and finite). Same definition and outputs as oracle_attend. */
+int oracle_attend_fp8kv(int is_global, int Hq, int Hkv, int hd, int window, double scale,
+                        int B, const int32_t *q_lens, const int32_t *ctx_lens, const int32_t *k_starts,
+                        const uint16_t *q, const uint8_t *k, const uint8_t *v, double k_scale, double v_scale,
+                        double *out, double *lse);
+
+/* Value of an E4M3 code (NaN for 0x7f and 0xff). */
+double oracle_e4m3_value(uint8_t code);
+
+/* Nearest E4M3 code to x, ties to the even code; finite magnitudes above 448 give +-448, NaN gives
+ * 0x7f with x's sign bit. */
+uint8_t oracle_e4m3_encode(float x);
+void oracle_e4m3_encode_n(int64_t n, const float *x, uint8_t *out);
+
+/* oracle_kv_append into E4M3 pools: each element is stored as oracle_e4m3_encode of the fp32
+ * quotient bf16_value / scale (k_scale for K, v_scale for V). */
+int64_t oracle_kv_append_fp8(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
+                             const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
+                             const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool, uint8_t *v_pool);
+
 /* OpenMP threads the oracle runs with. */
 int oracle_threads(void);
 

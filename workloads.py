@@ -135,6 +135,7 @@ class Batch:
     k_pool: np.ndarray          # uint16 [num_pages][Hkv][P][hd]
     v_pool: Optional[np.ndarray]
     meta: dict = field(default_factory=dict)
+    fp8: Optional["Fp8Kv"] = None  # an E4M3 copy of K/V (both sides), see with_fp8_kv
 
     @property
     def B(self) -> int:
@@ -170,10 +171,50 @@ class Batch:
             kk, vv = self.row_keys(r)
             ks.append(kk)
             vs.append(vv)
+        fp8 = None
+        if self.fp8 is not None:
+            offs = np.concatenate([[0], np.cumsum(self.ctx_lens - self.k_starts)])
+            f = self.fp8
+            fp8 = replace(f, k=np.concatenate([f.k[offs[r]:offs[r + 1]] for r in rows]),
+                          v=np.concatenate([f.v[offs[r]:offs[r + 1]] for r in rows]))
         return Batch(self.spec, self.ctx_lens[rows].copy(), self.q_lens[rows].copy(),
                      self.k_starts[rows].copy(), np.concatenate(qs), np.concatenate(ks),
                      None if self.v is None else np.concatenate(vs),
-                     self.page_table[rows].copy(), self.k_pool, self.v_pool, dict(self.meta))
+                     self.page_table[rows].copy(), self.k_pool, self.v_pool, dict(self.meta), fp8)
+
+
+@dataclass
+class Fp8Kv:
+    """An E4M3 (one byte per element) copy of a batch's K and V, on both sides: code c stands for
+    value(c) * k_scale in K and value(c) * v_scale in V."""
+    k: np.ndarray               # uint8, shaped like Batch.k
+    v: np.ndarray               # uint8, shaped like Batch.v
+    k_pool: np.ndarray          # uint8 [num_pages][Hkv][P][hd]
+    v_pool: np.ndarray
+    k_scale: float
+    v_scale: float
+
+
+# Scales of the FP8 copies: float32 values, not powers of two, different for K and V.
+FP8_K_SCALE = float(np.float32(0.0371))
+FP8_V_SCALE = float(np.float32(0.0213))
+
+
+def e4m3_codes(bf16_bits: np.ndarray, scale: float) -> np.ndarray:
+    """Input drawing only: E4M3 codes of bf16 values divided by ``scale`` (float32), by torch's
+    float8_e4m3fn cast. NaN (poisoned slots) gives a NaN code."""
+    import torch
+    x = bf16_bits_to_f32(bf16_bits) / np.float32(scale)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def with_fp8_kv(b: Batch, k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE) -> Batch:
+    """Attach an E4M3 copy of the batch's K/V (contiguous rows and pools, element by element, so
+    the two sides hold the same codes). Needs separate K and V."""
+    assert b.v is not None and b.v_pool is not None
+    b.fp8 = Fp8Kv(e4m3_codes(b.k, k_scale), e4m3_codes(b.v, v_scale), e4m3_codes(b.k_pool, k_scale),
+                  e4m3_codes(b.v_pool, v_scale), float(k_scale), float(v_scale))
+    return b
 
 
 def first_needed_token(spec: LayerSpec, ctx_len: int, q_len: int) -> int:
