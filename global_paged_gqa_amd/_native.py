@@ -82,6 +82,9 @@ _lib.gattn_decode_workspace_bytes.argtypes = [ctypes.POINTER(Layer), c_int, c_in
 _lib.gattn_decode.restype = c_int
 _lib.gattn_decode.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_int, c_int,
                               c_int, c_vp, c_size, c_vp, c_vp, c_vp]
+_lib.gattn_decode_fp8kv.restype = c_int
+_lib.gattn_decode_fp8kv.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_float, c_float, c_i64, c_vp, c_int,
+                                    c_vp, c_int, c_int, c_int, c_vp, c_size, c_vp, c_vp, c_vp]
 _lib.gattn_prefill.restype = c_int
 _lib.gattn_prefill.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_vp, c_int,
                                c_int, c_vp, c_vp, c_vp]
@@ -127,6 +130,15 @@ def gattn_decode(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, ctx
     _check(rc, "gattn_decode")
 
 
+def gattn_decode_fp8kv(layer, q, k_pool, v_pool, k_scale, v_scale, num_pages, page_table, pt_stride, ctx_lens,
+                       batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream=None):
+    rc = _lib.gattn_decode_fp8kv(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), float(k_scale),
+                                 float(v_scale), int(num_pages), _addr(page_table), int(pt_stride), _addr(ctx_lens),
+                                 int(batch), int(max_ctx), int(split_tokens), _addr(workspace), int(workspace_bytes),
+                                 _addr(out), _addr(lse), _stream(stream))
+    _check(rc, "gattn_decode_fp8kv")
+
+
 def gattn_prefill(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, cu_q, ctx_lens, batch, max_q,
                   out, lse, stream=None):
     rc = _lib.gattn_prefill(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), int(num_pages),
@@ -152,6 +164,6 @@ def gattn_combine(batch, num_q_heads, head_dim, num_splits, o_part, lse_part, ou
 def exported_symbols():
     """Names the shared library exports (for the ABI check)."""
     return sorted(n for n in ("gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
-                              "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine",
-                              "gattn_kv_append")
+                              "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
+                              "gattn_combine", "gattn_kv_append")
                   if hasattr(_lib, n))

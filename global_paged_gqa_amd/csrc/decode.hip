@@ -31,6 +31,19 @@
 // The g query heads sharing the KV head fill the 16 MFMA columns (padding heads have
 // zero queries and are never written). At the end the wave states merge through LDS in a
 // fixed order, so the result does not depend on timing or on the batch.
+//
+// FP8 pools (the opt-in FP8 KV pool for the sliding family of the pegainfer "[Model] Gemma 4
+// M2 26B-A4B" plan). K and V elements are OCP E4M3 bytes standing for value * k_scale and
+// value * v_scale. A page unit is half as many bytes and is staged the same way; each 16-byte
+// LDS chunk then holds 16 dims instead of 8. Every code is widened exactly to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: E4M3 values are a subset of bf16), so the MFMAs
+// are the bf16 ones:
+//   K: one 16-byte chunk read gives a lane two K-steps' operands (dims 64 j + 16 r4 + 0..7 and
+//      8..15); Q^T is loaded in the same dim order.
+//   V: the same transpose read returns 2-byte elements, now two adjacent dims of four tokens;
+//      two byte permutes split them into one 4-token word per dim, so output tile 2T + h holds
+//      dims 32 T + 2 c + h.
+// k_scale is folded into the score scale and v_scale into the final normalisation.
 #include "common.h"
 #include "kernels.h"
 
@@ -40,7 +53,13 @@ namespace {
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-template <int HD, bool SHARED, int W, int DS, int kSliceBytes>
+// Four E4M3 codes -> four bf16 values (exact), low word first.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+template <int HD, bool SHARED, int W, int DS, int kSliceBytes, bool F8 = false>
 __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a) {
     // W page streams of DS waves each; a wave streams its share of the head dims of its
     // stream's pages through its own kSliceBytes of LDS
@@ -49,15 +68,16 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     constexpr int kRingBytes = kWaves * kSliceBytes;
     constexpr int NKS = HD / 32 / DS;            // K-steps of 32 dims in the wave's score partial
     constexpr int NDT = HD / 16 / DS;            // 16-dim output tiles of the wave
+    constexpr int ESZ = F8 ? 1 : 2;              // bytes per K/V element
     constexpr int SEG = HD / DS;                 // head dims per wave
-    constexpr int SEGB = SEG * 2;                // bytes of a token row's segment
-    constexpr int PAGEB = kPage * HD * 2;        // bytes of one page's K (or V), one KV head
+    constexpr int SEGB = SEG * ESZ;              // bytes of a token row's segment
+    constexpr int PAGEB = kPage * HD * ESZ;      // bytes of one page's K (or V), one KV head
     constexpr int UNIT = kPage * SEGB;           // the wave's segment of it
     constexpr int UPP = SHARED ? 1 : 2;          // units per page
     constexpr int SUB = kSliceBytes;
     constexpr int NU = SUB / UNIT;               // units in a slice
     constexpr int LPU = UNIT / 1024;             // 1 KB load instructions per unit
-    constexpr int CPR = SEG / 8;                 // 16-byte chunks per segment row
+    constexpr int CPR = SEGB / 16;               // 16-byte chunks per segment row
     // The score of a page is always formed as NCH partial products over consecutive quarters
     // (halves at head_dim 256) of the head dims, added in a fixed tree, whatever DS is: a wave
     // holds NCH / DS of them, so the sum, and everything after it, has the same bits for any DS.
@@ -68,6 +88,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     static_assert(NU >= 2, "decode ring shape");
     static_assert(NU * LPU + 1 <= 63, "vmcnt range");
     static_assert(16 * HD * 4 <= DS * kSliceBytes, "merge buffer");
+    static_assert(!F8 || (DS == 1 && !SHARED), "fp8 pools: one wave per page, separate K and V");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
     __shared__ float sm_m[W][16];
@@ -117,13 +138,14 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     int ids_base = 0;
 
     // ---- Q^T as the B operand of the score product: lane holds head c16 (zeros past g),
-    // dims SEG dq + 32 s + 8 r4 .. +7
+    // dims SEG dq + 32 s + 8 r4 .. +7 (FP8: 64 (s / 2) + 16 r4 + 8 (s % 2) .. +7)
     u32x4 qb[NKS];
     {
-        const uint16_t *qp = a.q + ((int64_t)b * Hq + kvh * g + min(c16, g - 1)) * HD + SEG * dq + 8 * r4;
+        const uint16_t *qp = a.q + ((int64_t)b * Hq + kvh * g + min(c16, g - 1)) * HD + SEG * dq +
+                             (F8 ? 16 : 8) * r4;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            const u32x4 v = *(const u32x4 *)(qp + 32 * s);
+            const u32x4 v = *(const u32x4 *)(qp + (F8 ? 64 * (s >> 1) + 8 * (s & 1) : 32 * s));
             qb[s] = c16 < g ? v : u32x4{0, 0, 0, 0};
         }
     }
@@ -132,6 +154,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     // index, so operand offsets repeat with a period of 16 chunks (256 bytes) and the rest of
     // each offset is an immediate.
     // K operand (step s): token c16, logical chunk 4 s + r4 -> kbase[s % 4] + 256 (s / 4)
+    // (FP8: chunk 4 j + r4 feeds steps 2 j and 2 j + 1)
     uint32_t kbase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -152,7 +175,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     auto src_off = [&](int i) {
         const int P = 64 * i + lane;
         const int t = P / CPR;
-        return (uint32_t)(t * HD * 2 + SEGB * dq + ((P % CPR) ^ dswz(t)) * 16);
+        return (uint32_t)(t * HD * ESZ + SEGB * dq + ((P % CPR) ^ dswz(t)) * 16);
     };
 
     f32x4 acc[NDT];
@@ -184,8 +207,8 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
         }
         if (!live)
             pid = 0;
-        const uint16_t *pool = (SHARED || (u & 1) == 0) ? a.k_pool : a.v_pool;
-        const u32x4 rs = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * (kPage * HD), live ? PAGEB : 0);
+        const uint8_t *pool = (const uint8_t *)((SHARED || (u & 1) == 0) ? a.k_pool : a.v_pool);
+        const u32x4 rs = raw_rsrc(pool + ((int64_t)pid * a.num_kv_heads + kvh) * PAGEB, live ? PAGEB : 0);
         const uint32_t dst = sub_lds + (uint32_t)((u % NU) * UNIT);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -212,13 +235,31 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
             ch[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (F8) {
+            // chunk j holds the operands of steps 2 j (its low 8 bytes) and 2 j + 1
+            u32x4 kc[NKS / 2];
 #pragma unroll
-        for (int i = 0; i < NKS / CPW; ++i)
+            for (int j = 0; j < NKS / 2; ++j)
+                kc[j] = *(const u32x4 *)(ks + kbase[j & 3] + 256 * (j >> 2));
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const int s = c * (NKS / CPW) + i;
-                ch[c] = mfma_k32(*(const u32x4 *)(ks + kbase[s & 3] + 256 * (s >> 2)), qb[s], ch[c]);
-            }
+            for (int i = 0; i < NKS / CPW; ++i)
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) {
+                    const int s = c * (NKS / CPW) + i;
+                    const u32x4 w = kc[s >> 1];
+                    const u32x2 lo = e4m3x4_to_bf16((s & 1) ? w[2] : w[0]);
+                    const u32x2 hi = e4m3x4_to_bf16((s & 1) ? w[3] : w[1]);
+                    ch[c] = mfma_k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, qb[s], ch[c]);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NKS / CPW; ++i)
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) {
+                    const int s = c * (NKS / CPW) + i;
+                    ch[c] = mfma_k32(*(const u32x4 *)(ks + kbase[s & 3] + 256 * (s >> 2)), qb[s], ch[c]);
+                }
+        }
         f32x4 st;
         if constexpr (CPW == 4)
             st = (ch[0] + ch[1]) + (ch[2] + ch[3]);
@@ -292,9 +333,20 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
                     *(u32x4 *)(vs + r * SEGB + lane * 16) = u32x4{0, 0, 0, 0};
             }
         }
+        if constexpr (F8) {
+            // read T: element c16 of the tile is dims 32 T + 2 c16 (low byte) and + 1 of four tokens
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            acc[dt] = mfma_k16(tr_read(vs + vbase[dt & 7] + 256 * (dt >> 3)), pb, acc[dt]);
+            for (int T = 0; T < NDT / 2; ++T) {
+                const u32x2 w = tr_read(vs + vbase[T & 7] + 256 * (T >> 3));
+                acc[2 * T] = mfma_k16(e4m3x4_to_bf16(__builtin_amdgcn_perm(w[1], w[0], 0x06040200u)), pb, acc[2 * T]);
+                acc[2 * T + 1] =
+                    mfma_k16(e4m3x4_to_bf16(__builtin_amdgcn_perm(w[1], w[0], 0x07050301u)), pb, acc[2 * T + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[dt] = mfma_k16(tr_read(vs + vbase[dt & 7] + 256 * (dt >> 3)), pb, acc[dt]);
+        }
         issue(uv + NU);
         u = uv + 1;
     }
@@ -322,10 +374,21 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
             M = fmaxf(M, sm_m[w][c16]);
         const float cw = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
         if (c16 < g) {
-            float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 4 * r4;
+            if constexpr (F8) {
+                // tiles 2T and 2T + 1 interleave: element i of each is dim 32 T + 8 r4 + 2 i (+ 1)
+                float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 8 * r4;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                *(f32x4 *)(dst + 16 * dt) = acc[dt] * cw;
+                for (int T = 0; T < NDT / 2; ++T) {
+                    const f32x4 e = acc[2 * T] * cw, o = acc[2 * T + 1] * cw;
+                    *(f32x4 *)(dst + 32 * T) = f32x4{e[0], o[0], e[1], o[1]};
+                    *(f32x4 *)(dst + 32 * T + 4) = f32x4{e[2], o[2], e[3], o[3]};
+                }
+            } else {
+                float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 4 * r4;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    *(f32x4 *)(dst + 16 * dt) = acc[dt] * cw;
+            }
         }
     }
     __syncthreads();
@@ -349,7 +412,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
             lxsum += cw * sm_lx[w][hn];
             o += *(const f32x4 *)(mo + ((size_t)w * g + hn) * HD + d);
         }
-        const float inv = 1.0f / lsum;
+        const float inv = F8 ? a.v_scale / lsum : 1.0f / lsum;
         float lse = (M + fast_log2(lxsum)) * kLn2;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -412,6 +475,17 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, int batch, hipStream_t stream) {
+    if (head_dim != 256)
+        return hipErrorInvalidValue;
+    const dim3 grid(a.n_slots, a.num_kv_heads, batch);
+    constexpr int W = DecodeShape<256>::waves;
+    constexpr int SLICE = DecodeShape<256>::slice;
+    void *args[] = {(void *)&a};
+    return hipLaunchKernel((const void *)decode_split_kernel<256, false, W, 1, SLICE, true>, grid, dim3(W * 64),
+                           args, 0, stream);
+}
 
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                hipStream_t stream) {

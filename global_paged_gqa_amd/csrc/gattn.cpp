@@ -120,13 +120,24 @@ size_t gattn_decode_workspace_bytes(const gattn_layer *layer, int batch, int max
     return workspace_for(layer, batch, p);
 }
 
-int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
-                 int64_t num_pages, const int32_t *page_table, int pt_stride, const int32_t *ctx_lens,
-                 int batch, int max_ctx, int split_tokens, void *workspace, size_t workspace_bytes,
-                 uint16_t *out, float *lse, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode over bf16 pools, or over E4M3 pools (fp8) with their per-tensor scales.
+int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool, const void *v_pool, bool fp8,
+                float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
+                size_t workspace_bytes, uint16_t *out, float *lse, void *stream) {
     int rc = check_layer(layer);
     if (rc != GATTN_OK)
         return rc;
+    if (fp8) {
+        if (layer->head_dim != 256 || layer->kv_shared)
+            return GATTN_ERR_UNSUPPORTED;
+        if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+            return GATTN_ERR_BAD_SHAPE;
+    }
     if (batch < 0 || max_ctx < 1 || pt_stride < 1 || num_pages < 1)
         return GATTN_ERR_BAD_SHAPE;
     if ((int64_t)pt_stride * GATTN_PAGE_SIZE < (int64_t)max_ctx)
@@ -169,6 +180,11 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
     a.n_slots = plan.n_slots;
     a.max_ctx = max_ctx;
     a.scale_log2 = layer->scale * 1.4426950408889634f;
+    a.v_scale = 1.0f;
+    if (fp8) {
+        a.scale_log2 *= k_scale;
+        a.v_scale = v_scale;
+    }
     a.out = out;
     a.lse = lse;
     if (plan.n_slots > 1) {
@@ -177,7 +193,9 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
         a.lse_part = (float *)workspace + n_o;
     }
     hipStream_t s = (hipStream_t)stream;
-    if (gattn::launch_decode_split(a, layer->head_dim, layer->kv_shared != 0, batch, s) != hipSuccess)
+    const hipError_t e = fp8 ? gattn::launch_decode_split_fp8(a, layer->head_dim, batch, s)
+                             : gattn::launch_decode_split(a, layer->head_dim, layer->kv_shared != 0, batch, s);
+    if (e != hipSuccess)
         return GATTN_ERR_HIP;
     if (plan.n_slots > 1) {
         if (gattn::launch_combine(batch, layer->num_q_heads, layer->head_dim, plan.n_slots, a.o_part,
@@ -185,6 +203,26 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
             return GATTN_ERR_HIP;
     }
     return GATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                 int64_t num_pages, const int32_t *page_table, int pt_stride, const int32_t *ctx_lens,
+                 int batch, int max_ctx, int split_tokens, void *workspace, size_t workspace_bytes,
+                 uint16_t *out, float *lse, void *stream) {
+    return decode_impl(layer, q, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride, ctx_lens,
+                       batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream);
+}
+
+int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                       float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                       const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
+                       size_t workspace_bytes, uint16_t *out, float *lse, void *stream) {
+    return decode_impl(layer, q, k_pool, v_pool, true, k_scale, v_scale, num_pages, page_table, pt_stride, ctx_lens,
+                       batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream);
 }
 
 int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,

@@ -8,8 +8,8 @@ namespace gattn {
 
 struct DecodeArgs {
     const uint16_t *q;
-    const uint16_t *k_pool;
-    const uint16_t *v_pool;
+    const void *k_pool;  // bf16, or E4M3 bytes for the FP8 kernel
+    const void *v_pool;
     const int32_t *page_table;
     const int32_t *ctx_lens;
     float *o_part;     // per-split partials (several splits per row)
@@ -23,7 +23,8 @@ struct DecodeArgs {
     int split_tokens;  // keys per split
     int n_slots;       // splits per row the grid covers
     int max_ctx;
-    float scale_log2;  // softmax scale times log2(e)
+    float scale_log2;  // softmax scale times log2(e) (times k_scale for FP8 pools)
+    float v_scale;     // FP8 pools: the V scale (multiplies the normalised output)
 };
 
 struct PrefillArgs {
@@ -62,6 +63,9 @@ hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, hipStr
 
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                hipStream_t stream);
+
+// Decode over E4M3 pools (head_dim 256, separate K and V pools).
+hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, int batch, hipStream_t stream);
 
 hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);

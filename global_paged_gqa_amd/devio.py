@@ -49,20 +49,35 @@ class DeviceBatch:
         self.lse = torch.empty((T, s.num_q_heads), dtype=torch.float32, device="cuda")
         self.workspace = None
         self.ws_bytes = 0
+        f = getattr(batch, "fp8", None)
+        self.k_pool8 = None if f is None else dev(f.k_pool)
+        self.v_pool8 = None if f is None else dev(f.v_pool)
 
-    def decode(self, split_tokens, max_ctx=None, stream=None, poison_workspace=True):
-        b = self.batch
-        B = b.B
-        max_ctx = int(b.ctx_lens.max()) if max_ctx is None else int(max_ctx)
-        need = nat.gattn_decode_workspace_bytes(self.layer, B, max_ctx, split_tokens)
+    def _workspace(self, split_tokens, max_ctx, poison_workspace):
+        need = nat.gattn_decode_workspace_bytes(self.layer, self.batch.B, max_ctx, split_tokens)
         if need > self.ws_bytes:
             self.workspace = torch.empty(need // 4, dtype=torch.float32, device="cuda")
             self.ws_bytes = need
             if poison_workspace:
                 self.workspace.fill_(float("nan"))
+
+    def decode(self, split_tokens, max_ctx=None, stream=None, poison_workspace=True):
+        b = self.batch
+        B = b.B
+        max_ctx = int(b.ctx_lens.max()) if max_ctx is None else int(max_ctx)
+        self._workspace(split_tokens, max_ctx, poison_workspace)
         nat.gattn_decode(self.layer, self.q, self.k_pool, self.v_pool, self.num_pages, self.page_table,
                          self.pt_stride, self.ctx_lens, B, max_ctx, split_tokens, self.workspace, self.ws_bytes,
                          self.out, self.lse, stream)
+
+    def decode_fp8(self, split_tokens, max_ctx=None, stream=None, poison_workspace=True):
+        """gattn_decode_fp8kv over the batch's E4M3 pools (Batch.fp8)."""
+        b = self.batch
+        max_ctx = int(b.ctx_lens.max()) if max_ctx is None else int(max_ctx)
+        self._workspace(split_tokens, max_ctx, poison_workspace)
+        nat.gattn_decode_fp8kv(self.layer, self.q, self.k_pool8, self.v_pool8, b.fp8.k_scale, b.fp8.v_scale,
+                               self.num_pages, self.page_table, self.pt_stride, self.ctx_lens, b.B, max_ctx,
+                               split_tokens, self.workspace, self.ws_bytes, self.out, self.lse, stream)
 
     def prefill(self, max_q=None, stream=None):
         b = self.batch
@@ -78,6 +93,12 @@ class DeviceBatch:
 def decode(batch, split_tokens, max_ctx=None):
     d = DeviceBatch(batch)
     d.decode(split_tokens, max_ctx)
+    return d.result()
+
+
+def decode_fp8(batch, split_tokens, max_ctx=None):
+    d = DeviceBatch(batch)
+    d.decode_fp8(split_tokens, max_ctx)
     return d.result()
 
 

@@ -158,6 +158,27 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
                  size_t workspace_bytes, uint16_t *out, float *lse, void *stream);
 
 /*
+ * gattn_decode over an FP8 KV pool (the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan's opt-in
+ * FP8 KV pool for the sliding family; the vLLM Gemma 4 recipe serves with "--kv-cache-dtype
+ * fp8"). Halves the bytes a decode step reads.
+ *
+ *   k_pool, v_pool  [num_pages][num_kv_heads][16][head_dim] bytes (the layout above with
+ *              one-byte elements), each an OCP E4M3 code: sign, 4 exponent bits (bias 7), 3
+ *              mantissa bits, subnormals at exponent 0, 0x7f / 0xff NaN, no infinities,
+ *              largest magnitude 448. Separate pools (layer->kv_shared must be 0).
+ *   k_scale, v_scale  one positive finite scale per tensor: a stored K code c stands for
+ *              value(c) * k_scale, a V code for value(c) * v_scale.
+ * Everything else (q, page table, lengths, split policy, workspace size and layout, outputs,
+ * errors, fail-closed rows) is exactly as for gattn_decode; the result is attention over the
+ * dequantized K and V. Served for head_dim 256 (the local family's); other layers return
+ * GATTN_ERR_UNSUPPORTED, a scale that is not positive and finite GATTN_ERR_BAD_SHAPE.
+ */
+int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                       float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                       const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
+                       size_t workspace_bytes, uint16_t *out, float *lse, void *stream);
+
+/*
  * Chunked causal prefill (Core AI card, "Contents": a flash-prefill with a
  * query axis and an intra-chunk causal mask; "hybrid-pf64/ bundles": a prefill
  * entrypoint next to decode). Row r has q_len = cu_q[r+1] - cu_q[r] queries at

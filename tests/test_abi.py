@@ -27,8 +27,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
-                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_prefill", "gattn_combine",
-                            "gattn_kv_append"])
+                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
+                            "gattn_combine", "gattn_kv_append"])
     for n in names:
         assert hasattr(nat._lib, n), n
     assert g.gattn_abi_version() == 1
@@ -189,6 +189,33 @@ def test_kv_append_rejects_bad_arguments():
     assert st(shared, **dict(ok, v_new=None, v_pool=3)) == 0          # v_pool == k_pool
     assert st(shared, **dict(ok, v_new=2, v_pool=None)) == nat.ERR_BAD_SHAPE
     assert st(shared, **dict(ok, v_new=None, v_pool=4)) == nat.ERR_BAD_SHAPE
+
+
+def test_decode_fp8kv_rejects_bad_arguments():
+    """The FP8-pool decode validates like gattn_decode, serves head_dim 256 with separate K and V
+    pools only, and needs positive finite scales; batch 0 with valid arguments is a no-op."""
+    lay = g.make_layer("local", 32, 16, 256, window=1024)
+    ok = dict(q=1, k_pool=2, v_pool=3, k_scale=0.5, v_scale=0.25, num_pages=10, page_table=4, pt_stride=8,
+              ctx_lens=5, batch=0, max_ctx=128, split_tokens=64, workspace=None, workspace_bytes=0, out=6, lse=7)
+
+    def st(layer, **kw):
+        try:
+            g.gattn_decode_fp8kv(layer, **kw, stream=0)
+        except g.GattnError as e:
+            return e.status
+        return 0
+    assert st(lay, **ok) == 0
+    for key in ("q", "k_pool", "v_pool", "page_table", "ctx_lens", "out", "lse"):
+        assert st(lay, **dict(ok, **{key: None})) == nat.ERR_NULL_PTR, key
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert st(lay, **dict(ok, k_scale=bad)) == nat.ERR_BAD_SHAPE, bad
+        assert st(lay, **dict(ok, v_scale=bad)) == nat.ERR_BAD_SHAPE, bad
+    assert st(g.make_layer("global", 32, 4, 512), **ok) == nat.ERR_UNSUPPORTED
+    assert st(g.make_layer("local", 32, 16, 256, window=1024, kv_shared=True), **ok) == nat.ERR_UNSUPPORTED
+    assert st(lay, **dict(ok, split_tokens=24)) == nat.ERR_BAD_SPLIT
+    assert st(lay, **dict(ok, batch=2)) == nat.ERR_WORKSPACE_TOO_SMALL  # several splits need the workspace
+    assert st(lay, **dict(ok, max_ctx=0)) == nat.ERR_BAD_SHAPE
+    assert st(g.make_layer("global", 8, 2, 256), **ok) == 0  # any family at head_dim 256
 
 
 def test_one_hip_runtime_in_process():

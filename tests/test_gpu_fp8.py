@@ -1,0 +1,113 @@
+"""Decode over an FP8 (E4M3) KV pool on the GPU against the fp64 oracle over the dequantized
+K/V (O max-abs 1e-2, LSE max-abs 1e-3): local rows at window edges and across many windows,
+every split policy, the 12B local geometry, a head_dim 256 global layer, the full local decode
+batch, poisoned never-visible slots and fail-closed rows."""
+import numpy as np
+import pytest
+
+import __graft_entry__
+
+__graft_entry__.ensure_built()
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def devio():
+    import torch
+    assert torch.cuda.is_available()
+    from global_paged_gqa_amd import devio as d
+    return d
+
+
+def check(ref, out, lse, tag):
+    ref_o, ref_l = ref
+    eo = float(np.max(np.abs(out - ref_o)))
+    el = float(np.max(np.abs(lse - ref_l)))
+    print(f"{tag}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    assert eo <= TOL_O and el <= TOL_LSE, (tag, eo, el)
+
+
+def _local_rows(key, n=14, hi=9000):
+    L = workloads.ragged(key, 1, hi, n)
+    L[:8] = [1, 15, 16, 17, 1023, 1024, 1025, 2049]
+    return L
+
+
+@pytest.mark.parametrize("split", [512, 1024, 256, 0])
+def test_fp8_local_decode(devio, split):
+    spec = workloads.LOCAL_31B
+    L = _local_rows((81, 1))
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (81, 1), back="visible", poison=True,
+                             extra_pages=2)
+    workloads.with_fp8_kv(b)
+    out, lse = devio.decode_fp8(b, split)
+    check(oracle.attend_batch(b), out, lse, f"fp8 local decode split {split}")
+
+
+def test_fp8_local_decode_12b(devio):
+    spec = workloads.LOCAL_12B
+    L = _local_rows((81, 2), n=10)
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (81, 2), back="visible", poison=True)
+    workloads.with_fp8_kv(b, 0.05, 0.0125)
+    out, lse = devio.decode_fp8(b, 512)
+    check(oracle.attend_batch(b), out, lse, "fp8 12B local decode")
+
+
+@pytest.mark.parametrize("split", [512, 0])
+def test_fp8_global_family_at_head_dim_256(devio, split):
+    """The kernel is family-agnostic: a full-causal layer at head_dim 256, g = 4."""
+    spec = workloads.LayerSpec("global", 8, 2, 256)
+    L = workloads.ragged((81, 3), 1, 5000, 6)
+    L[0] = 1
+    b = workloads.make_batch(spec, L, np.ones(6, np.int32), (81, 3), back="visible", poison=True)
+    workloads.with_fp8_kv(b)
+    out, lse = devio.decode_fp8(b, split)
+    check(oracle.attend_batch(b), out, lse, f"fp8 global hd256 split {split}")
+
+
+def test_fp8_local_decode_full_batch(devio):
+    """The local decode workload at full size (64 rows, 512 .. 32768 tokens, split 512)."""
+    b = workloads.cfg3_local_decode()
+    workloads.with_fp8_kv(b)
+    out, lse = devio.decode_fp8(b, 512)
+    check(oracle.attend_batch(b), out, lse, "fp8 local decode B=64")
+
+
+def test_fp8_scales_reach_scores_and_output(devio):
+    """Scales changed after the codes were drawn: K codes standing for 4x larger values (sharper
+    softmax), V codes for half as large ones. Dropping or swapping a scale moves the LSE and O far
+    beyond the tolerance."""
+    spec = workloads.LOCAL_31B
+    L = np.array([700, 1500, 33], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(3, np.int32), (81, 4), back="visible", poison=True)
+    workloads.with_fp8_kv(b, 0.025, 0.0213)
+    b.fp8.k_scale, b.fp8.v_scale = 0.1, 0.01065
+    out, lse = devio.decode_fp8(b, 512)
+    check(oracle.attend_batch(b), out, lse, "fp8 rescaled")
+
+
+def test_fp8_decode_fails_closed(devio):
+    """A visible page id out of range in one row turns that row's outputs into NaN; the other rows
+    are unaffected."""
+    import torch
+    spec = workloads.LOCAL_31B
+    L = np.array([900, 2000, 40], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(3, np.int32), (81, 5), back="visible")
+    workloads.with_fp8_kv(b)
+    d = devio.DeviceBatch(b)
+    pt = b.page_table.copy()
+    pt[1, (L[1] - 1) // 16] = b.num_pages
+    d.page_table = devio.dev(pt)
+    d.decode_fp8(512)
+    out, lse = d.result()
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
+    ref = oracle.attend_batch(b, rows=[0, 2])
+    check(ref, out[[0, 2]], lse[[0, 2]], "fp8 fail-closed neighbours")
+    torch.cuda.synchronize()

@@ -205,6 +205,8 @@ def e4m3_codes(bf16_bits: np.ndarray, scale: float) -> np.ndarray:
     float8_e4m3fn cast. NaN (poisoned slots) gives a NaN code."""
     import torch
     x = bf16_bits_to_f32(bf16_bits) / np.float32(scale)
+    # torch's cast turns finite values beyond the format's range into NaN: the scale must avoid that
+    assert not np.any(np.isfinite(x) & (np.abs(x) >= 464)), "scale too small for E4M3"
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
