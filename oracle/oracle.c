@@ -429,6 +429,15 @@ int oracle_threads(void)
 #endif
 }
 
+/* E4M3 code of the fp32 quotient x / scale (scale > 0). The sign is x's: for a number it is the
+ * quotient's sign anyway, and a NaN x stores NaN with its own sign bit. */
+static uint8_t encode_quotient(float x, float scale)
+{
+    if (isnan(x))
+        return signbit(x) ? 0xff : 0x7f;
+    return oracle_e4m3_encode(x / scale);
+}
+
 /* Destination of the new tokens: bf16 pools (k_pool, v_pool) or E4M3 pools (k_pool8, v_pool8) with
  * their scales. */
 typedef struct {
@@ -468,11 +477,10 @@ static int64_t append_rows(int Hkv, int hd, int page_size, int B, const int32_t 
                     const int64_t dst = ((page * Hkv + kv) * page_size + slot) * hd + d;
                     const int64_t src = (src_tok * Hkv + kv) * hd + d;
                     if (fp8) {
-                        /* the fp32 quotient, rounded to E4M3 */
-                        dst_pools->k_pool8[dst] = oracle_e4m3_encode((float)widen_bf16(k_new[src]) / dst_pools->k_scale);
+                        dst_pools->k_pool8[dst] = encode_quotient((float)widen_bf16(k_new[src]), dst_pools->k_scale);
                         if (v_new)
                             dst_pools->v_pool8[dst] =
-                                oracle_e4m3_encode((float)widen_bf16(v_new[src]) / dst_pools->v_scale);
+                                encode_quotient((float)widen_bf16(v_new[src]), dst_pools->v_scale);
                     } else {
                         dst_pools->k_pool[dst] = k_new[src];
                         if (v_new)

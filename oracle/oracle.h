@@ -73,7 +73,8 @@ uint8_t oracle_e4m3_encode(float x);
 void oracle_e4m3_encode_n(int64_t n, const float *x, uint8_t *out);
 
 /* oracle_kv_append into E4M3 pools: each element is stored as oracle_e4m3_encode of the fp32
- * quotient bf16_value / scale (k_scale for K, v_scale for V). */
+ * quotient bf16_value / scale (k_scale for K, v_scale for V); a NaN value stores NaN with its own
+ * sign bit. */
 int64_t oracle_kv_append_fp8(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
                              const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
                              const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool, uint8_t *v_pool);

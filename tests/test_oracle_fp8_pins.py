@@ -161,3 +161,17 @@ def test_kv_append_fp8_is_the_bf16_append_then_the_encoder():
     qv = workloads.bf16_bits_to_f32(vpb) / np.float32(vs)
     assert np.array_equal(kp8, np.where(written, oracle.e4m3_encode(qk), k8))
     assert np.array_equal(vp8, np.where(written, oracle.e4m3_encode(qv), v8))
+
+
+def test_kv_append_fp8_special_values():
+    """NaN keeps its sign, infinities saturate to +-448, -0 stays -0, whatever the scale."""
+    Hkv, hd, P = 1, 8, 16
+    vals = np.array([0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80, 0x8000, 0x0000, 0x3F80], np.uint16)  # bf16 bits
+    k_new = vals.reshape(1, Hkv, hd)
+    pool = np.zeros((1, Hkv, P, hd), np.uint8)
+    for ks in (1.0, 0.0371, 1e-30):
+        kp, _, skipped = oracle.kv_append_fp8(Hkv, hd, P, [0, 1], [1], np.zeros((1, 1), np.int32), 1, k_new, None,
+                                              ks, 1.0, pool, None)
+        one = oracle.e4m3_encode(np.array([1.0 / np.float32(ks)], np.float32))[0]
+        assert skipped == 0
+        assert list(kp[0, 0, 0]) == [0x7F, 0xFF, 0x7F, 0x7E, 0xFE, 0x80, 0x00, one], ks
