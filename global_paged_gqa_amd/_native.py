@@ -91,6 +91,9 @@ _lib.gattn_prefill.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c
 _lib.gattn_kv_append.restype = c_int
 _lib.gattn_kv_append.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_vp,
                                  c_int, c_int, c_vp, c_vp]
+_lib.gattn_kv_append_fp8.restype = c_int
+_lib.gattn_kv_append_fp8.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_vp, c_float, c_float, c_i64, c_vp,
+                                     c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp]
 _lib.gattn_combine.restype = c_int
 _lib.gattn_combine.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]
 
@@ -155,6 +158,15 @@ def gattn_kv_append(layer, k_new, v_new, k_pool, v_pool, num_pages, page_table, 
     _check(rc, "gattn_kv_append")
 
 
+def gattn_kv_append_fp8(layer, k_new, v_new, k_pool, v_pool, k_scale, v_scale, num_pages, page_table, pt_stride,
+                        cu_new, ctx_lens, batch, max_new, status=None, stream=None):
+    rc = _lib.gattn_kv_append_fp8(ctypes.byref(layer), _addr(k_new), _addr(v_new), _addr(k_pool), _addr(v_pool),
+                                  float(k_scale), float(v_scale), int(num_pages), _addr(page_table), int(pt_stride),
+                                  _addr(cu_new), _addr(ctx_lens), int(batch), int(max_new), _addr(status),
+                                  _stream(stream))
+    _check(rc, "gattn_kv_append_fp8")
+
+
 def gattn_combine(batch, num_q_heads, head_dim, num_splits, o_part, lse_part, out, lse, stream=None):
     rc = _lib.gattn_combine(int(batch), int(num_q_heads), int(head_dim), int(num_splits), _addr(o_part),
                             _addr(lse_part), _addr(out), _addr(lse), _stream(stream))
@@ -165,5 +177,5 @@ def exported_symbols():
     """Names the shared library exports (for the ABI check)."""
     return sorted(n for n in ("gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
                               "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
-                              "gattn_combine", "gattn_kv_append")
+                              "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8")
                   if hasattr(_lib, n))

@@ -9,6 +9,11 @@
 // every wave reads and writes whole contiguous rows with several loads in flight, and a row's
 // page id is looked up once per row. It is a pure copy, bound by HBM bandwidth: 2 * head_dim * 2 bytes read and
 // written per (token, kv_head) and pool (K, and V unless V is the K cache).
+//
+// Into an FP8 (E4M3) pool (the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan's opt-in FP8 KV pool)
+// each element is stored as the code nearest to the fp32 quotient value / scale (IEEE division),
+// ties to the even code, magnitudes of 448 and above saturating to 448, NaN kept as NaN; a lane's
+// 16 source bytes become 8 pool bytes.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,7 +25,32 @@ constexpr int kThreads = 256;
 constexpr int kTok = 4;     // tokens per workgroup
 constexpr int kUnroll = 4;  // rows a lane loads before it stores them (loads in flight)
 
-template <int HD>
+// E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits) of the fp32 quotient x / scale
+// (scale > 0): nearest, ties to even, saturating at 448; the sign is x's (a NaN keeps it too).
+__device__ __forceinline__ uint32_t e4m3_code(float x, float scale) {
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+    const uint32_t a = __builtin_bit_cast(uint32_t, x / scale) & 0x7fffffffu;
+    if (a > 0x7f800000u)  // NaN
+        return sign | 0x7fu;
+    if (a >= 0x43e00000u)  // |quotient| >= 448, infinities included
+        return sign | 0x7eu;
+    if (a < 0x3c800000u)  // below 2^-6: subnormal steps of 2^-9; the scaling by 2^9 is exact
+        return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+    const uint32_t mant = a & 0x7fffffu;
+    uint32_t code = (((a >> 23) - 120u) << 3) | (mant >> 20);  // exponent rebiased 127 -> 7
+    const uint32_t rest = mant & 0xfffffu;                      // the 20 bits rounded away
+    if (rest > 0x80000u || (rest == 0x80000u && (code & 1u)))
+        ++code;  // a carry into the exponent is the correct next binade; below 448 code stays <= 0x7e
+    return sign | code;
+}
+
+// Four bf16 values (two packed words) -> four E4M3 bytes of value / scale, first value lowest.
+__device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float scale) {
+    return e4m3_code(bf16_lo(w0), scale) | (e4m3_code(bf16_hi(w0), scale) << 8) |
+           (e4m3_code(bf16_lo(w1), scale) << 16) | (e4m3_code(bf16_hi(w1), scale) << 24);
+}
+
+template <int HD, bool F8>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     constexpr int CPR = HD / 8;           // 16-byte chunks per (token, kv_head) row
     constexpr int RPI = kThreads / CPR;   // rows a workgroup copies per step
@@ -54,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
             }
             const int64_t src = ((int64_t)(n0 + i0 + it) * Hkv + kvh) * HD + c * 8;
             dst[u] = (((int64_t)pid * Hkv + kvh) * kPage + (t & (kPage - 1))) * HD + c * 8;
-            kv[u] = *(const u32x4 *)(a.k_new + src);
+            kv[u] = *(const u32x4 *)(a.k_new + src);  // dst is an element offset (bytes for FP8)
             if (a.v_new)
                 vv[u] = *(const u32x4 *)(a.v_new + src);
         }
@@ -62,9 +92,20 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
         for (int u = 0; u < kUnroll; ++u) {
             if (dst[u] < 0)
                 continue;
-            *(u32x4 *)(a.k_pool + dst[u]) = kv[u];
-            if (a.v_new)
-                *(u32x4 *)(a.v_pool + dst[u]) = vv[u];
+            if constexpr (F8) {
+                const u32x4 k = kv[u];
+                *(u32x2 *)((uint8_t *)a.k_pool + dst[u]) =
+                    u32x2{e4m3x4(k[0], k[1], a.k_scale), e4m3x4(k[2], k[3], a.k_scale)};
+                if (a.v_new) {
+                    const u32x4 v = vv[u];
+                    *(u32x2 *)((uint8_t *)a.v_pool + dst[u]) =
+                        u32x2{e4m3x4(v[0], v[1], a.v_scale), e4m3x4(v[2], v[3], a.v_scale)};
+                }
+            } else {
+                *(u32x4 *)((uint16_t *)a.k_pool + dst[u]) = kv[u];
+                if (a.v_new)
+                    *(u32x4 *)((uint16_t *)a.v_pool + dst[u]) = vv[u];
+            }
         }
     }
     if (a.status && __builtin_amdgcn_ballot_w64(bad) && (threadIdx.x & 63) == 0)
@@ -73,13 +114,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 
 }  // namespace
 
-hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, hipStream_t stream) {
+hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, bool fp8, hipStream_t stream) {
     const dim3 grid((a.max_new + kTok - 1) / kTok, batch);
     void *args[] = {(void *)&a};
+    if (fp8)
+        return head_dim == 256
+                   ? hipLaunchKernel((const void *)kv_append_kernel<256, true>, grid, dim3(kThreads), args, 0, stream)
+                   : hipErrorInvalidValue;
     if (head_dim == 256)
-        return hipLaunchKernel((const void *)kv_append_kernel<256>, grid, dim3(kThreads), args, 0, stream);
+        return hipLaunchKernel((const void *)kv_append_kernel<256, false>, grid, dim3(kThreads), args, 0, stream);
     if (head_dim == 512)
-        return hipLaunchKernel((const void *)kv_append_kernel<512>, grid, dim3(kThreads), args, 0, stream);
+        return hipLaunchKernel((const void *)kv_append_kernel<512, false>, grid, dim3(kThreads), args, 0, stream);
     return hipErrorInvalidValue;
 }
 

@@ -476,12 +476,16 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 
 }  // namespace
 
+// FP8 pools (4 KB units): two page streams of one wave with four units (two pages) each. A
+// workgroup then holds 32 KB of LDS and the wave's registers allow two waves per SIMD, so four
+// workgroups (eight waves, 128 KB of loads in flight) fit a CU; measured on the local decode
+// workload, 8% faster than the bf16 shape's 24 KB slices (three workgroups per CU), with the
+// same bits.
 hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, int batch, hipStream_t stream) {
     if (head_dim != 256)
         return hipErrorInvalidValue;
     const dim3 grid(a.n_slots, a.num_kv_heads, batch);
-    constexpr int W = DecodeShape<256>::waves;
-    constexpr int SLICE = DecodeShape<256>::slice;
+    constexpr int W = 2, SLICE = 16 * 1024;
     void *args[] = {(void *)&a};
     return hipLaunchKernel((const void *)decode_split_kernel<256, false, W, 1, SLICE, true>, grid, dim3(W * 64),
                            args, 0, stream);

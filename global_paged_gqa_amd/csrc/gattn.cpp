@@ -268,13 +268,24 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
     return GATTN_OK;
 }
 
-int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
-                    uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
-                    const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
-                    void *stream) {
+}  // extern "C"
+
+namespace {
+
+// KV append into bf16 pools, or into E4M3 pools (fp8) with their per-tensor scales.
+int append_impl(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, void *k_pool, void *v_pool,
+                bool fp8, float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
+                void *stream) {
     int rc = check_layer(layer);
     if (rc != GATTN_OK)
         return rc;
+    if (fp8) {
+        if (layer->head_dim != 256 || layer->kv_shared)
+            return GATTN_ERR_UNSUPPORTED;
+        if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+            return GATTN_ERR_BAD_SHAPE;
+    }
     if (batch < 0 || max_new < 0 || pt_stride < 1 || num_pages < 1)
         return GATTN_ERR_BAD_SHAPE;
     if (!k_new || !k_pool || !page_table || !cu_new || !ctx_lens)
@@ -301,9 +312,31 @@ int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint1
     a.pt_stride = pt_stride;
     a.num_kv_heads = layer->num_kv_heads;
     a.max_new = max_new;
-    if (gattn::launch_kv_append(a, layer->head_dim, batch, (hipStream_t)stream) != hipSuccess)
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    if (gattn::launch_kv_append(a, layer->head_dim, batch, fp8, (hipStream_t)stream) != hipSuccess)
         return GATTN_ERR_HIP;
     return GATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,
+                    uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                    const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
+                    void *stream) {
+    return append_impl(layer, k_new, v_new, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride,
+                       cu_new, ctx_lens, batch, max_new, status, stream);
+}
+
+int gattn_kv_append_fp8(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool,
+                        uint8_t *v_pool, float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table,
+                        int pt_stride, const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new,
+                        int32_t *status, void *stream) {
+    return append_impl(layer, k_new, v_new, k_pool, v_pool, true, k_scale, v_scale, num_pages, page_table, pt_stride,
+                       cu_new, ctx_lens, batch, max_new, status, stream);
 }
 
 int gattn_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,

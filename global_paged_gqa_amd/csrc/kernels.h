@@ -47,8 +47,8 @@ struct PrefillArgs {
 struct AppendArgs {
     const uint16_t *k_new;
     const uint16_t *v_new;   // null: only K is written (V is the K cache)
-    uint16_t *k_pool;
-    uint16_t *v_pool;
+    void *k_pool;            // bf16, or E4M3 bytes for the FP8 kernel
+    void *v_pool;
     const int32_t *page_table;
     const int32_t *cu_new;
     const int32_t *ctx_lens;
@@ -57,9 +57,10 @@ struct AppendArgs {
     int pt_stride;
     int num_kv_heads;
     int max_new;
+    float k_scale, v_scale;  // FP8 pools: stored code = E4M3(value / scale)
 };
 
-hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, bool fp8, hipStream_t stream);
 
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                hipStream_t stream);

@@ -245,6 +245,21 @@ int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint1
                     const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new, int32_t *status,
                     void *stream);
 
+/*
+ * gattn_kv_append into an FP8 KV pool (the layout and codes of gattn_decode_fp8kv). Each new bf16
+ * element x is stored as the E4M3 code nearest to the fp32 quotient x / scale (IEEE division;
+ * k_scale for K, v_scale for V), ties to the even code; quotients of magnitude 448 or more (and
+ * infinities) store +-448, NaN stores NaN (0x7f with x's sign). The pages leave the rounding rule
+ * open; this one keeps every finite value finite. Rows, positions, the page table, fail-closed
+ * behaviour and status are exactly as for gattn_kv_append. Served for head_dim 256 with separate
+ * K and V (layer->kv_shared 0; v_new and v_pool required); other layers return
+ * GATTN_ERR_UNSUPPORTED, a scale that is not positive and finite GATTN_ERR_BAD_SHAPE.
+ */
+int gattn_kv_append_fp8(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool,
+                        uint8_t *v_pool, float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table,
+                        int pt_stride, const int32_t *cu_new, const int32_t *ctx_lens, int batch, int max_new,
+                        int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
                             "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
-                            "gattn_combine", "gattn_kv_append"])
+                            "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8"])
     for n in names:
         assert hasattr(nat._lib, n), n
     assert g.gattn_abi_version() == 1
@@ -216,6 +216,29 @@ def test_decode_fp8kv_rejects_bad_arguments():
     assert st(lay, **dict(ok, batch=2)) == nat.ERR_WORKSPACE_TOO_SMALL  # several splits need the workspace
     assert st(lay, **dict(ok, max_ctx=0)) == nat.ERR_BAD_SHAPE
     assert st(g.make_layer("global", 8, 2, 256), **ok) == 0  # any family at head_dim 256
+
+
+def test_kv_append_fp8_rejects_bad_arguments():
+    lay = g.make_layer("local", 32, 16, 256, window=1024)
+    ok = dict(k_new=1, v_new=2, k_pool=3, v_pool=4, k_scale=0.5, v_scale=0.25, num_pages=10, page_table=5,
+              pt_stride=8, cu_new=6, ctx_lens=7, batch=0, max_new=16, status=None)
+
+    def st(layer, **kw):
+        try:
+            g.gattn_kv_append_fp8(layer, **kw, stream=0)
+        except g.GattnError as e:
+            return e.status
+        return 0
+    assert st(lay, **ok) == 0
+    for key in ("k_new", "v_new", "k_pool", "v_pool", "page_table", "cu_new", "ctx_lens"):
+        assert st(lay, **dict(ok, **{key: None})) == nat.ERR_NULL_PTR, key
+    for bad in (0.0, -2.0, math.inf, math.nan):
+        assert st(lay, **dict(ok, k_scale=bad)) == nat.ERR_BAD_SHAPE, bad
+        assert st(lay, **dict(ok, v_scale=bad)) == nat.ERR_BAD_SHAPE, bad
+    assert st(g.make_layer("global", 32, 4, 512), **ok) == nat.ERR_UNSUPPORTED
+    assert st(g.make_layer("local", 32, 16, 256, window=1024, kv_shared=True), **ok) == nat.ERR_UNSUPPORTED
+    assert st(lay, **dict(ok, batch=-1)) == nat.ERR_BAD_SHAPE
+    assert st(lay, **dict(ok, num_pages=0)) == nat.ERR_BAD_SHAPE
 
 
 def test_one_hip_runtime_in_process():

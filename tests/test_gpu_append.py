@@ -119,3 +119,112 @@ def test_append_then_prefill(devio, spec):
     ref_o, ref_l = oracle.attend_batch(b)
     assert int(status.item()) == 0
     assert np.max(np.abs(out - ref_o)) <= 1e-2 and np.max(np.abs(lse - ref_l)) <= 1e-3
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) pools
+def _run_fp8(devio, spec, b, L, n_new, cu, k_new, v_new, k8, v8, ks, vs, page_table=None):
+    import torch
+    nat = devio.nat
+    kp = torch.from_numpy(np.ascontiguousarray(k8)).to("cuda")
+    vp = torch.from_numpy(np.ascontiguousarray(v8)).to("cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pt = b.page_table if page_table is None else page_table
+    nat.gattn_kv_append_fp8(devio.layer_of(spec), devio.dev(k_new), devio.dev(v_new), kp, vp, ks, vs, b.num_pages,
+                            devio.dev(pt.astype(np.int32)), pt.shape[1], devio.dev(cu), devio.dev(L), b.B,
+                            int(n_new.max()), status)
+    torch.cuda.synchronize()
+    return kp.cpu().numpy(), vp.cpu().numpy(), int(status.item())
+
+
+@pytest.mark.parametrize("ks,vs", [(0.5, 2.0 ** -7), (0.0371, 0.0213)], ids=["dyadic", "non-dyadic"])
+def test_kv_append_fp8_every_bf16_value(devio, ks, vs):
+    """All 65536 bf16 bit patterns (NaN, infinities, subnormals, exact midpoints under the dyadic
+    scales) appended into E4M3 pools: every byte equals the oracle's encoder output."""
+    spec = workloads.LOCAL_31B
+    Hkv, hd = spec.num_kv_heads, spec.head_dim
+    T = 65536 // (Hkv * hd)                   # 16 tokens hold every pattern once
+    L = np.array([T + 5, 1], np.int32)
+    n_new = np.array([T, 0], np.int32)
+    cu = np.array([0, T, T], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(2, np.int32), (44, 0), back="all", extra_pages=1)
+    k_new = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, hd)
+    v_new = np.ascontiguousarray(k_new[::-1])
+    g = np.random.default_rng(44)
+    k8 = g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    v8 = g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    kp, vp, status = _run_fp8(devio, spec, b, L, n_new, cu, k_new, v_new, k8, v8, ks, vs)
+    ref_k, ref_v, skipped = oracle.kv_append_fp8(Hkv, hd, spec.page_size, cu, L, b.page_table, b.num_pages, k_new,
+                                                 v_new, ks, vs, k8, v8)
+    assert skipped == 0 and status == 0
+    assert np.array_equal(kp, ref_k) and np.array_equal(vp, ref_v)
+
+
+@pytest.mark.parametrize("spec", [workloads.LOCAL_31B, workloads.LOCAL_12B], ids=["31b", "12b"])
+def test_kv_append_fp8_bitwise_and_fails_closed(devio, spec):
+    """Ragged rows (0, 1, a page, page-crossing, a 2048-token chunk), a bad page id and a row with
+    more new tokens than cached ones: bytes equal the oracle's, the status flag rises."""
+    b, L, n_new, cu, k_new, v_new = _case(spec, (45, spec.num_kv_heads))
+    pt = b.page_table.copy()
+    pt[3, (L[3] - 1) // 16] = -1
+    L_bad = L.copy()
+    L_bad[4] = 3
+    g = np.random.default_rng(45)
+    k8 = g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    v8 = g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+    kp, vp, status = _run_fp8(devio, spec, b, L_bad, n_new, cu, k_new, v_new, k8, v8, ks, vs, page_table=pt)
+    ref_k, ref_v, skipped = oracle.kv_append_fp8(spec.num_kv_heads, spec.head_dim, spec.page_size, cu, L_bad, pt,
+                                                 b.num_pages, k_new, v_new, ks, vs, k8, v8)
+    assert skipped > 0 and status == 1
+    assert np.array_equal(kp, ref_k) and np.array_equal(vp, ref_v)
+
+
+def test_append_fp8_then_decode_fp8(devio):
+    """Decode rows whose last tokens were just appended into NaN-filled E4M3 slots: the decode over
+    the pool the append built matches the oracle over the oracle-appended codes."""
+    import torch
+    spec = workloads.LOCAL_31B
+    L = np.array([1, 17, 1024, 1500, 3000], np.int32)
+    C = np.array([1, 17, 300, 1, 64], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(5, np.int32), (46, 1), back="visible")
+    workloads.with_fp8_kv(b)
+    f = b.fp8
+    cu = np.concatenate([[0], np.cumsum(C)]).astype(np.int32)
+    k_new, v_new = [], []
+    for r in range(b.B):
+        kk, vv = b.row_keys(r)
+        k_new.append(kk[len(kk) - C[r]:])
+        v_new.append(vv[len(vv) - C[r]:])
+    k_new, v_new = np.concatenate(k_new), np.concatenate(v_new)
+    k8, v8 = f.k_pool.copy(), f.v_pool.copy()
+    for r in range(b.B):  # the appended slots hold NaN codes before the append
+        for t in range(L[r] - C[r], L[r]):
+            k8[b.page_table[r, t // 16], :, t % 16, :] = 0x7F
+            v8[b.page_table[r, t // 16], :, t % 16, :] = 0xFF
+    ref_k, ref_v, skipped = oracle.kv_append_fp8(spec.num_kv_heads, spec.head_dim, 16, cu, L, b.page_table,
+                                                 b.num_pages, k_new, v_new, f.k_scale, f.v_scale, k8, v8)
+    assert skipped == 0
+    d = devio.DeviceBatch(b)
+    d.k_pool8 = torch.from_numpy(k8).to("cuda")
+    d.v_pool8 = torch.from_numpy(v8).to("cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    devio.nat.gattn_kv_append_fp8(d.layer, devio.dev(k_new), devio.dev(v_new), d.k_pool8, d.v_pool8, f.k_scale,
+                                  f.v_scale, b.num_pages, d.page_table, b.pt_stride, devio.dev(cu), d.ctx_lens, b.B,
+                                  int(C.max()), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(d.k_pool8.cpu().numpy(), ref_k) and np.array_equal(d.v_pool8.cpu().numpy(), ref_v)
+    d.decode_fp8(512)
+    out, lse = d.result()
+    # the oracle side: the contiguous rows re-gathered from the oracle-appended pools
+    P = 16
+    ks8, vs8 = [], []
+    for r in range(b.B):
+        toks = np.arange(int(b.k_starts[r]), int(L[r]))
+        ks8.append(ref_k[b.page_table[r, toks // P], :, toks % P, :])
+        vs8.append(ref_v[b.page_table[r, toks // P], :, toks % P, :])
+    ref_o, ref_l = oracle.attend_fp8kv(False, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.window,
+                                       spec.softmax_scale, b.q_lens, b.ctx_lens, b.k_starts, b.q,
+                                       np.concatenate(ks8), np.concatenate(vs8), f.k_scale, f.v_scale)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    assert np.max(np.abs(out - ref_o)) <= 1e-2 and np.max(np.abs(lse - ref_l)) <= 1e-3
