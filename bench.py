@@ -178,6 +178,21 @@ def append_measure(torch, devio, workloads, stream, flush, iters=20):
         t = median(event_times(torch, stream, call, iters, flush))
         out[fam] = {"tokens": int(sum(kn.shape[0] for _, _, kn, _, _, _ in rows)), "bytes": nbytes,
                     "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1)}
+        if fam == "local":  # the same tokens into E4M3 pools: 2 bytes read and 1 written per element
+            pools8 = [(torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda"),
+                       torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")) for d, *_ in rows]
+            nbytes8 = sum(kn.numel() * (2 + 1) * 2 for _, _, kn, _, _, _ in rows)
+
+            def call8():
+                for (d, cu, kn, vn, B, mx), (k8, v8) in zip(rows, pools8):
+                    devio.nat.gattn_kv_append_fp8(d.layer, kn, vn, k8, v8, workloads.FP8_K_SCALE,
+                                                  workloads.FP8_V_SCALE, d.num_pages, d.page_table, d.pt_stride, cu,
+                                                  d.ctx_lens, B, mx, None)
+            for _ in range(5):
+                call8()
+            t8 = median(event_times(torch, stream, call8, iters, flush))
+            out["local_fp8"] = {"bytes": nbytes8, "us": round(t8 * 1e6, 2), "gbs": round(nbytes8 / t8 / 1e9, 1)}
+            del pools8
         del rows
     out["workload"] = ("gattn_kv_append of the mixed step's 8252 new tokens per family (4 prefill chunks of 2048, "
                        "60 decode tokens) into the 31B pools, two calls")
@@ -218,10 +233,22 @@ def local_decode_measure(torch, devio, workloads, traffic, stream, flush, steps=
         d.decode(512)
     t = median(event_times(torch, stream, lambda: d.decode(512), steps))
     tf = median(event_times(torch, stream, lambda: d.decode(512), 10, flush))
-    return {"workload": "local decode: batch 64, 32 q heads, 16 KV heads, hd 256, window 1024, contexts "
-                        "~U{512..32768}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
-            "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
-            "mall_flushed_gbs": round(kv / tf / 1e9, 1)}
+    out = {"workload": "local decode: batch 64, 32 q heads, 16 KV heads, hd 256, window 1024, contexts "
+                       "~U{512..32768}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
+           "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
+           "mall_flushed_gbs": round(kv / tf / 1e9, 1)}
+    del d
+    # the same rows over an FP8 (E4M3) pool: half the bytes per visible key
+    d8 = devio.DeviceLayout(lay, workloads.fill_e4m3_device, fp8=(workloads.FP8_K_SCALE, workloads.FP8_V_SCALE))
+    kv8 = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, lay.ctx_lens, 1)
+    for _ in range(5):
+        d8.decode(512)
+    t8 = median(event_times(torch, stream, lambda: d8.decode(512), steps))
+    tf8 = median(event_times(torch, stream, lambda: d8.decode(512), 10, flush))
+    out["fp8"] = {"kv_bytes": kv8, "us": round(t8 * 1e6, 2), "gbs": round(kv8 / t8 / 1e9, 1),
+                  "frac": round(kv8 / t8 / 1e9 / HBM_PEAK_GBS, 4), "mall_flushed_us": round(tf8 * 1e6, 2),
+                  "mall_flushed_gbs": round(kv8 / tf8 / 1e9, 1), "speedup_vs_bf16": round(t / t8, 3)}
+    return out
 
 
 def gemma12b_measure(torch, devio, workloads, traffic, stream, flush, steps=50):

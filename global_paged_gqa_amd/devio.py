@@ -116,17 +116,27 @@ class DeviceLayout:
     workspace may be shared between layouts that run one after another on one stream.
     """
 
-    def __init__(self, lay, fill, workspace=None):
+    def __init__(self, lay, fill, workspace=None, fp8=None):
+        """fp8 = (k_scale, v_scale): E4M3 pools (one byte per element) filled by
+        ``fill(tensor, seed, scale)``, read by gattn_decode_fp8kv; no host rows."""
         s = lay.spec
         self.lay = lay
         self.layer = layer_of(s)
+        self.fp8 = fp8
         shape = (lay.num_pages, s.num_kv_heads, s.page_size, s.head_dim)
-        self.k_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
-        fill(self.k_pool, lay.fill_seed)
-        self.v_pool = None
-        if not s.kv_shared:
-            self.v_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
-            fill(self.v_pool, lay.fill_seed + 1)
+        if fp8 is not None:
+            assert not lay.rows and not s.kv_shared
+            self.k_pool = torch.empty(shape, dtype=torch.uint8, device="cuda")
+            self.v_pool = torch.empty(shape, dtype=torch.uint8, device="cuda")
+            fill(self.k_pool, lay.fill_seed, fp8[0])
+            fill(self.v_pool, lay.fill_seed + 1, fp8[1])
+        else:
+            self.k_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
+            fill(self.k_pool, lay.fill_seed)
+            self.v_pool = None
+            if not s.kv_shared:
+                self.v_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
+                fill(self.v_pool, lay.fill_seed + 1)
         for r in lay.rows:
             pids = torch.from_numpy(lay.row_pages[r]).to("cuda")
             for pool, tok in ((self.k_pool, lay.k_tok.get(r)), (self.v_pool, lay.v_tok.get(r))):
@@ -153,6 +163,11 @@ class DeviceLayout:
         if need > self.ws_bytes:
             self.workspace = torch.empty(need // 4, dtype=torch.float32, device="cuda")
             self.ws_bytes = need
+        if self.fp8 is not None:
+            nat.gattn_decode_fp8kv(self.layer, self.q, self.k_pool, self.v_pool, self.fp8[0], self.fp8[1],
+                                   lay.num_pages, self.page_table, lay.pt_stride, self.ctx_lens, lay.B, max_ctx,
+                                   split_tokens, self.workspace, self.ws_bytes, self.out, self.lse, stream)
+            return
         nat.gattn_decode(self.layer, self.q, self.k_pool, self.v_pool, lay.num_pages, self.page_table,
                          lay.pt_stride, self.ctx_lens, lay.B, max_ctx, split_tokens, self.workspace, self.ws_bytes,
                          self.out, self.lse, stream)

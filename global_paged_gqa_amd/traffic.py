@@ -1,7 +1,8 @@
 """Algorithmic work of one call, for roofline figures (counting only, no attention math).
 
 Decode: every visible key's K (and V unless shared) is read once:
-    bytes = sum over rows and KV heads of n_visible * head_dim * 2 B * (1 if K=V else 2).
+    bytes = sum over rows and KV heads of n_visible * head_dim * e B * (1 if K=V else 2),
+    e = 2 for bf16 pools, 1 for FP8 (E4M3) pools.
 Prefill: flops = sum over visible (query, key) pairs of 4 * head_dim * num_q_heads
     (QK^T and PV, two flops per multiply-add, masked or skipped pairs not counted).
 A query at position p sees p + 1 keys (global) or min(p + 1, window) keys (local).
@@ -19,9 +20,9 @@ def n_visible(is_global: bool, window: int, pos) -> np.ndarray:
     return pos + 1 if is_global else np.minimum(pos + 1, window)
 
 
-def decode_kv_bytes(is_global, window, num_kv_heads, head_dim, kv_shared, ctx_lens) -> int:
+def decode_kv_bytes(is_global, window, num_kv_heads, head_dim, kv_shared, ctx_lens, elem_bytes: int = 2) -> int:
     n = int(n_visible(is_global, window, np.asarray(ctx_lens, np.int64) - 1).sum())
-    return n * num_kv_heads * head_dim * 2 * (1 if kv_shared else 2)
+    return n * num_kv_heads * head_dim * elem_bytes * (1 if kv_shared else 2)
 
 
 def prefill_flops(is_global, window, num_q_heads, head_dim, ctx_lens, q_lens) -> int:

@@ -492,6 +492,19 @@ def fill_normal_bf16_device(t, seed: int, chunk: int = 1 << 26) -> None:
         flat[s:e] = torch.randn(e - s, generator=g, device=t.device, dtype=torch.float32).to(torch.bfloat16)
 
 
+def fill_e4m3_device(t, seed: int, scale: float, chunk: int = 1 << 26) -> None:
+    """Fill a device uint8 tensor with E4M3 codes of N(0,1) / scale (torch's device generator and
+    float8_e4m3fn cast; values beyond the format's range are clamped first so no code is NaN)."""
+    import torch
+    flat = t.view(-1)
+    g = torch.Generator(device=t.device)
+    g.manual_seed(int(seed))
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        x = torch.randn(e - s, generator=g, device=t.device, dtype=torch.float32) / scale
+        flat[s:e] = x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
 def sweep_layer(layer: int, family: str, rows=()) -> PagedLayout:
     """Layer ``layer`` of the 60-layer decode sweep: 16 rows at 32768 tokens; global layers share
     K and V (head_dim 512, 4 KV heads), local layers are the 31B local family (window pages only)."""
