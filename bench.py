@@ -288,10 +288,11 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
     end to end and per family; then the 65536-token global K=V decode."""
     nat = devio.nat
     n = workloads.SWEEP_LAYERS
-    layers, kv_total, kv_fam = [], 0, {"local": 0, "global": 0}
+    layers, lays, kv_total, kv_fam = [], [], 0, {"local": 0, "global": 0}
     for l in range(n):
         fam = "global" if nat.gattn_layer_family(l, n) == nat.GLOBAL else "local"
         lay = workloads.sweep_layer(l, fam)
+        lays.append(lay)
         s = lay.spec
         kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, lay.ctx_lens)
         kv_total += kv
@@ -347,6 +348,27 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
     for fam in ("local", "global"):
         out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
         out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
+    # the same sweep with the 50 local layers' K/V in FP8 (E4M3) pools (gattn_decode_fp8kv): half their bytes
+    try:
+        layers8 = []
+        for (fam, d), lay in zip(layers, lays):
+            if fam == "local":
+                d = devio.DeviceLayout(lay, workloads.fill_e4m3_device, workspace=ws,
+                                       fp8=(workloads.FP8_K_SCALE, workloads.FP8_V_SCALE))
+            layers8.append((fam, d))
+
+        def sweep8():
+            for fam, d in layers8:
+                d.decode(workloads.SWEEP_SPLIT[fam])
+        sweep8()
+        torch.cuda.synchronize()
+        t8 = median(event_times(torch, stream, sweep8, reps))
+        kv8 = kv_fam["global"] + kv_fam["local"] // 2
+        out["fp8_local"] = {"kv_bytes": kv8, "ms": round(t8 * 1e3, 4), "gbs": round(kv8 / t8 / 1e9, 1),
+                            "speedup_vs_bf16": round(t / t8, 3)}
+        del layers8
+    except Exception as e:  # report, never hide
+        out["fp8_local"] = {"error": str(e)[:200]}
     del layers, ws
     torch.cuda.empty_cache()
 

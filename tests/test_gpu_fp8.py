@@ -111,3 +111,36 @@ def test_fp8_decode_fails_closed(devio):
     ref = oracle.attend_batch(b, rows=[0, 2])
     check(ref, out[[0, 2]], lse[[0, 2]], "fp8 fail-closed neighbours")
     torch.cuda.synchronize()
+
+
+def test_fp8_decode_graph_replay(devio):
+    """gattn_decode_fp8kv only enqueues kernels (split kernel and combine), so a capture replays:
+    three replays, each after eager work that overwrites every output, reproduce the eager result
+    bit for bit, and that matches the oracle."""
+    import torch
+    spec = workloads.LOCAL_31B
+    L = _local_rows((81, 6), n=9)
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (81, 6), back="visible", poison=True)
+    workloads.with_fp8_kv(b)
+    d = devio.DeviceBatch(b)
+    d.decode_fp8(512)  # eager; allocates the workspace before the capture
+    eager = d.result()
+    check(oracle.attend_batch(b), *eager, "fp8 eager before capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d.decode_fp8(512)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        d.decode_fp8(512)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        d.out.fill_(rep + 1)
+        d.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o, l = d.result()
+        assert np.array_equal(o, eager[0]) and np.array_equal(l, eager[1]), rep
