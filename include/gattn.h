@@ -19,7 +19,9 @@
  *
  * Data types. bf16 arrays are passed as uint16_t bit patterns (bfloat16,
  * round-to-nearest-even when the library produces them). LSE and split partials
- * are fp32. All arithmetic on the device accumulates in fp32.
+ * are fp32. All arithmetic on the device accumulates in fp32. The opt-in FP8 KV
+ * pool (gattn_decode_fp8kv, gattn_kv_append_fp8) holds one-byte E4M3 codes in the
+ * same layout, with one scale per tensor.
  *
  * KV pool layout (one pool per layer; K and V have separate pools unless shared):
  *   pool[num_pages][num_kv_heads][page_size][head_dim] bf16, page_size = 16.
