@@ -211,3 +211,14 @@ def test_prefill_bitwise_invariances(devio):
                           b.page_table[[2]], b.k_pool, b.v_pool)
     o5, l5 = devio.prefill(sub)
     assert np.array_equal(o5, o1[cq[2]:cq[3]]) and np.array_equal(l5, l1[cq[2]:cq[3]])
+
+
+@pytest.mark.parametrize("family", ["global", "local"])
+def test_mixed_step_single_launch(devio, family):
+    """A mixed step's prefill rows and q_len-1 decode rows as one batch in one gattn_prefill call:
+    every output against the oracle (decode rows at their full visible range)."""
+    pre, dec = workloads.cfg4_mixed(family, n_prefill=2, chunk=300, max_prior=1500, n_decode=10,
+                                    max_decode_len=3000)
+    mix = workloads.concat_batches(pre, dec)
+    out, lse = devio.prefill(mix)
+    check(mix, out, lse, tag=f"single-launch mixed {family}")

@@ -72,3 +72,20 @@ def test_sweep_layer_shapes():
     assert g.num_pages == 16 * 2048 and g.host is None and not g.k_tok
     l = workloads.sweep_layer(0, "local")
     assert l.num_pages == 16 * 64 and l.spec.window == 1024
+
+
+def test_concat_batches_keeps_every_row_and_page():
+    """The concatenated batch's pool gives back each row's contiguous K/V, its queries follow in
+    order, and b's page ids point past a's pool."""
+    pre, dec = workloads.cfg4_mixed("local", n_prefill=2, chunk=64, max_prior=300, n_decode=5, max_decode_len=900)
+    mix = workloads.concat_batches(pre, dec)
+    assert mix.B == pre.B + dec.B and mix.num_pages == pre.num_pages + dec.num_pages
+    assert np.array_equal(mix.q, np.concatenate([pre.q, dec.q]))
+    for r in range(mix.B):
+        kk, vv = mix.row_keys(r)
+        assert np.array_equal(workloads.gather_row_from_pool(mix, r, mix.k_pool), kk)
+        assert np.array_equal(workloads.gather_row_from_pool(mix, r, mix.v_pool), vv)
+    src = [(pre, r) for r in range(pre.B)] + [(dec, r) for r in range(dec.B)]
+    for r, (b, rr) in enumerate(src):
+        assert np.array_equal(mix.row_keys(r)[0], b.row_keys(rr)[0])
+    assert np.all(mix.page_table[pre.B:][mix.page_table[pre.B:] >= 0] >= pre.num_pages)

@@ -219,6 +219,21 @@ def with_fp8_kv(b: Batch, k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_S
     return b
 
 
+def concat_batches(a: Batch, b: Batch) -> Batch:
+    """One batch holding a's rows then b's (same layer): queries, contiguous K/V and pools
+    concatenated, b's page ids shifted past a's pool. Data plumbing only (a mixed step's prefill
+    and decode rows as one call)."""
+    assert a.spec == b.spec and a.fp8 is None and b.fp8 is None
+    stride = max(a.pt_stride, b.pt_stride)
+    pt = np.full((a.B + b.B, stride), -1, dtype=np.int32)
+    pt[:a.B, :a.pt_stride] = a.page_table
+    pt[a.B:, :b.pt_stride] = np.where(b.page_table >= 0, b.page_table + a.num_pages, -1)
+    cat = lambda x, y: None if x is None else np.concatenate([x, y])
+    return Batch(a.spec, cat(a.ctx_lens, b.ctx_lens), cat(a.q_lens, b.q_lens), cat(a.k_starts, b.k_starts),
+                 cat(a.q, b.q), cat(a.k, b.k), cat(a.v, b.v), pt, cat(a.k_pool, b.k_pool), cat(a.v_pool, b.v_pool),
+                 {"concat": (a.meta, b.meta)})
+
+
 def first_needed_token(spec: LayerSpec, ctx_len: int, q_len: int) -> int:
     """Earliest token any of the row's queries can see (0 for global rows)."""
     if spec.is_global:
