@@ -144,3 +144,41 @@ def test_fp8_decode_graph_replay(devio):
         torch.cuda.synchronize()
         o, l = d.result()
         assert np.array_equal(o, eager[0]) and np.array_equal(l, eager[1]), rep
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_decode_page_ids_past_4_gib(devio, fp8):
+    """The batch's pages moved to ids 70000 and up, i.e. past byte offset 2^32 of their pools
+    (about 9.2 GB per bf16 pool, 4.6 GB per FP8 pool): the 64-bit page addressing reads them, and
+    the pages below them, all NaN, are never touched."""
+    import torch
+    spec = workloads.LOCAL_31B
+    L = np.array([1, 1025, 3000, 700, 17], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (81, 7), back="visible", poison=True)
+    if fp8:
+        workloads.with_fp8_kv(b)
+    base = 70000
+    d = devio.DeviceBatch(b)
+    n_pages = base + b.num_pages
+    shape = (n_pages, spec.num_kv_heads, spec.page_size, spec.head_dim)
+    if fp8:
+        assert base * spec.num_kv_heads * spec.page_size * spec.head_dim > 2 ** 32
+        for name in ("k_pool8", "v_pool8"):
+            big = torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda")
+            big[base:] = getattr(d, name)
+            setattr(d, name, big)
+    else:
+        for name in ("k_pool", "v_pool"):
+            big = torch.full(shape, int(workloads.BF16_NAN), dtype=torch.int16, device="cuda")
+            big[base:] = getattr(d, name)
+            setattr(d, name, big)
+    d.page_table = devio.dev(np.where(b.page_table >= 0, b.page_table + base, -1).astype(np.int32))
+    d.num_pages = n_pages
+    if fp8:
+        d.decode_fp8(512)
+    else:
+        d.decode(512)
+    out, lse = d.result()
+    check(oracle.attend_batch(b), out, lse, f"{'fp8' if fp8 else 'bf16'} pages past 4 GiB")
+    del d
+    torch.cuda.empty_cache()
