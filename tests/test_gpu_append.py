@@ -228,3 +228,46 @@ def test_append_fp8_then_decode_fp8(devio):
                                        np.concatenate(ks8), np.concatenate(vs8), f.k_scale, f.v_scale)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     assert np.max(np.abs(out - ref_o)) <= 1e-2 and np.max(np.abs(lse - ref_l)) <= 1e-3
+
+
+def test_append_and_prefill_past_4_gib(devio):
+    """Page ids from 70000 up (past byte offset 2^32 of each bf16 pool): the append writes the
+    chunk's K/V there and the prefill reads them back; the pages below stay NaN and untouched."""
+    import torch
+    spec = workloads.LOCAL_31B
+    L = np.array([700, 1500], np.int32)
+    C = np.array([200, 300], np.int32)
+    b = workloads.make_batch(spec, L, C, (47, 1), back="visible")
+    cu = np.concatenate([[0], np.cumsum(C)]).astype(np.int32)
+    k_new, v_new = [], []
+    for r in range(b.B):
+        kk, vv = b.row_keys(r)
+        k_new.append(kk[len(kk) - C[r]:])
+        v_new.append(vv[len(vv) - C[r]:])
+    k_new, v_new = np.concatenate(k_new), np.concatenate(v_new)
+    for r in range(b.B):  # the chunk's slots hold NaN before the append
+        for t in range(L[r] - C[r], L[r]):
+            b.k_pool[b.page_table[r, t // 16], :, t % 16, :] = workloads.BF16_NAN
+            b.v_pool[b.page_table[r, t // 16], :, t % 16, :] = workloads.BF16_NAN
+    base = 70000
+    d = devio.DeviceBatch(b)
+    n_pages = base + b.num_pages
+    shape = (n_pages, spec.num_kv_heads, spec.page_size, spec.head_dim)
+    for name in ("k_pool", "v_pool"):
+        big = torch.full(shape, int(workloads.BF16_NAN), dtype=torch.int16, device="cuda")
+        big[base:] = getattr(d, name)
+        setattr(d, name, big)
+    d.page_table = devio.dev(np.where(b.page_table >= 0, b.page_table + base, -1).astype(np.int32))
+    d.num_pages = n_pages
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    devio.nat.gattn_kv_append(d.layer, devio.dev(k_new), devio.dev(v_new), d.k_pool, d.v_pool, n_pages, d.page_table,
+                              b.pt_stride, devio.dev(cu), d.ctx_lens, b.B, int(C.max()), status)
+    d.prefill()
+    out, lse = d.result()
+    assert int(status.item()) == 0
+    low = d.k_pool[:base].view(-1)
+    assert bool((low == int(workloads.BF16_NAN)).all())
+    ref_o, ref_l = oracle.attend_batch(b)
+    assert np.max(np.abs(out - ref_o)) <= 1e-2 and np.max(np.abs(lse - ref_l)) <= 1e-3
+    del d, low
+    torch.cuda.empty_cache()
