@@ -117,10 +117,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
 hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, bool fp8, hipStream_t stream) {
     const dim3 grid((a.max_new + kTok - 1) / kTok, batch);
     void *args[] = {(void *)&a};
-    if (fp8)
-        return head_dim == 256
-                   ? hipLaunchKernel((const void *)kv_append_kernel<256, true>, grid, dim3(kThreads), args, 0, stream)
-                   : hipErrorInvalidValue;
+    if (fp8) {
+        if (head_dim == 256)
+            return hipLaunchKernel((const void *)kv_append_kernel<256, true>, grid, dim3(kThreads), args, 0, stream);
+        if (head_dim == 512)
+            return hipLaunchKernel((const void *)kv_append_kernel<512, true>, grid, dim3(kThreads), args, 0, stream);
+        return hipErrorInvalidValue;
+    }
     if (head_dim == 256)
         return hipLaunchKernel((const void *)kv_append_kernel<256, false>, grid, dim3(kThreads), args, 0, stream);
     if (head_dim == 512)

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     static_assert(NU >= 2, "decode ring shape");
     static_assert(NU * LPU + 1 <= 63, "vmcnt range");
     static_assert(16 * HD * 4 <= DS * kSliceBytes, "merge buffer");
-    static_assert(!F8 || (DS == 1 && !SHARED), "fp8 pools: one wave per page, separate K and V");
+    static_assert(!F8 || DS == 1, "fp8 pools: whole head dims per wave");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
     __shared__ float sm_m[W][16];
@@ -476,19 +476,27 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 
 }  // namespace
 
-// FP8 pools (4 KB units): two page streams of one wave with four units (two pages) each. A
-// workgroup then holds 32 KB of LDS and the wave's registers allow two waves per SIMD, so four
-// workgroups (eight waves, 128 KB of loads in flight) fit a CU; measured on the local decode
-// workload, 8% faster than the bf16 shape's 24 KB slices (three workgroups per CU), with the
-// same bits.
-hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, int batch, hipStream_t stream) {
-    if (head_dim != 256)
-        return hipErrorInvalidValue;
+// FP8 pools at head_dim 256 (4 KB units): two page streams of one wave with four units (two pages)
+// each. A workgroup then holds 32 KB of LDS and the wave's registers allow two waves per SIMD, so
+// four workgroups (eight waves, 128 KB of loads in flight) fit a CU; measured on the local decode
+// workload, 8% faster than the bf16 shape's 24 KB slices (three workgroups per CU), with the same
+// bits. At head_dim 512 (8 KB units) the bf16 shape: one wave, 32 KB.
+hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
+                                   hipStream_t stream) {
     const dim3 grid(a.n_slots, a.num_kv_heads, batch);
-    constexpr int W = 2, SLICE = 16 * 1024;
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)decode_split_kernel<256, false, W, 1, SLICE, true>, grid, dim3(W * 64),
-                           args, 0, stream);
+    const void *k = nullptr;
+    int threads = 64;
+    if (head_dim == 256 && !kv_shared) {
+        k = (const void *)decode_split_kernel<256, false, 2, 1, 16 * 1024, true>;
+        threads = 128;
+    } else if (head_dim == 512) {
+        k = kv_shared ? (const void *)decode_split_kernel<512, true, 1, 1, 32 * 1024, true>
+                      : (const void *)decode_split_kernel<512, false, 1, 1, 32 * 1024, true>;
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(k, grid, dim3(threads), args, 0, stream);
 }
 
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,

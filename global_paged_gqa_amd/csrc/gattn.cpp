@@ -133,9 +133,13 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
     if (rc != GATTN_OK)
         return rc;
     if (fp8) {
-        if (layer->head_dim != 256 || layer->kv_shared)
+        if (layer->head_dim == 256 && layer->kv_shared)
             return GATTN_ERR_UNSUPPORTED;
-        if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        if (!(k_scale > 0.0f) || !isfinite(k_scale))
+            return GATTN_ERR_BAD_SHAPE;
+        if (layer->kv_shared)
+            v_scale = k_scale;  // V is the K cache: its codes carry the K scale
+        else if (!(v_scale > 0.0f) || !isfinite(v_scale))
             return GATTN_ERR_BAD_SHAPE;
     }
     if (batch < 0 || max_ctx < 1 || pt_stride < 1 || num_pages < 1)
@@ -193,7 +197,7 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
         a.lse_part = (float *)workspace + n_o;
     }
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = fp8 ? gattn::launch_decode_split_fp8(a, layer->head_dim, batch, s)
+    const hipError_t e = fp8 ? gattn::launch_decode_split_fp8(a, layer->head_dim, layer->kv_shared != 0, batch, s)
                              : gattn::launch_decode_split(a, layer->head_dim, layer->kv_shared != 0, batch, s);
     if (e != hipSuccess)
         return GATTN_ERR_HIP;
@@ -281,9 +285,13 @@ int append_impl(const gattn_layer *layer, const uint16_t *k_new, const uint16_t 
     if (rc != GATTN_OK)
         return rc;
     if (fp8) {
-        if (layer->head_dim != 256 || layer->kv_shared)
+        if (layer->head_dim == 256 && layer->kv_shared)
             return GATTN_ERR_UNSUPPORTED;
-        if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        if (!(k_scale > 0.0f) || !isfinite(k_scale))
+            return GATTN_ERR_BAD_SHAPE;
+        if (layer->kv_shared)
+            v_scale = k_scale;  // unused: only K is written
+        else if (!(v_scale > 0.0f) || !isfinite(v_scale))
             return GATTN_ERR_BAD_SHAPE;
     }
     if (batch < 0 || max_new < 0 || pt_stride < 1 || num_pages < 1)

@@ -65,8 +65,9 @@ hipError_t launch_kv_append(const AppendArgs &a, int head_dim, int batch, bool f
 hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                hipStream_t stream);
 
-// Decode over E4M3 pools (head_dim 256, separate K and V pools).
-hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, int batch, hipStream_t stream);
+// Decode over E4M3 pools (head_dim 256 with separate K and V pools, or head_dim 512).
+hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
+                                   hipStream_t stream);
 
 hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);

@@ -51,7 +51,7 @@ class DeviceBatch:
         self.ws_bytes = 0
         f = getattr(batch, "fp8", None)
         self.k_pool8 = None if f is None else dev(f.k_pool)
-        self.v_pool8 = None if f is None else dev(f.v_pool)
+        self.v_pool8 = None if f is None or f.v_pool is None else dev(f.v_pool)
 
     def _workspace(self, split_tokens, max_ctx, poison_workspace):
         need = nat.gattn_decode_workspace_bytes(self.layer, self.batch.B, max_ctx, split_tokens)
@@ -125,11 +125,13 @@ class DeviceLayout:
         self.fp8 = fp8
         shape = (lay.num_pages, s.num_kv_heads, s.page_size, s.head_dim)
         if fp8 is not None:
-            assert not lay.rows and not s.kv_shared
+            assert not lay.rows
             self.k_pool = torch.empty(shape, dtype=torch.uint8, device="cuda")
-            self.v_pool = torch.empty(shape, dtype=torch.uint8, device="cuda")
             fill(self.k_pool, lay.fill_seed, fp8[0])
-            fill(self.v_pool, lay.fill_seed + 1, fp8[1])
+            self.v_pool = None
+            if not s.kv_shared:
+                self.v_pool = torch.empty(shape, dtype=torch.uint8, device="cuda")
+                fill(self.v_pool, lay.fill_seed + 1, fp8[1])
         else:
             self.k_pool = torch.empty(shape, dtype=torch.int16, device="cuda")
             fill(self.k_pool, lay.fill_seed)

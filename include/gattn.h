@@ -167,13 +167,16 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
  *   k_pool, v_pool  [num_pages][num_kv_heads][16][head_dim] bytes (the layout above with
  *              one-byte elements), each an OCP E4M3 code: sign, 4 exponent bits (bias 7), 3
  *              mantissa bits, subnormals at exponent 0, 0x7f / 0xff NaN, no infinities,
- *              largest magnitude 448. Separate pools (layer->kv_shared must be 0).
+ *              largest magnitude 448. With layer->kv_shared, v_pool is NULL or equal to k_pool.
  *   k_scale, v_scale  one positive finite scale per tensor: a stored K code c stands for
- *              value(c) * k_scale, a V code for value(c) * v_scale.
+ *              value(c) * k_scale, a V code for value(c) * v_scale. With layer->kv_shared, V is
+ *              the K cache and uses k_scale (v_scale is ignored).
  * Everything else (q, page table, lengths, split policy, workspace size and layout, outputs,
  * errors, fail-closed rows) is exactly as for gattn_decode; the result is attention over the
- * dequantized K and V. Served for head_dim 256 (the local family's); other layers return
- * GATTN_ERR_UNSUPPORTED, a scale that is not positive and finite GATTN_ERR_BAD_SHAPE.
+ * dequantized K and V. Served for head_dim 256 with separate pools (the local family) and for
+ * head_dim 512 with or without K=V (the global family: the vLLM recipe's FP8 cache covers every
+ * layer); a head_dim 256 layer with kv_shared returns GATTN_ERR_UNSUPPORTED, a scale that is not
+ * positive and finite GATTN_ERR_BAD_SHAPE.
  */
 int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
                        float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
@@ -253,9 +256,10 @@ int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint1
  * k_scale for K, v_scale for V), ties to the even code; quotients of magnitude 448 or more (and
  * infinities) store +-448, NaN stores NaN (0x7f with x's sign). The pages leave the rounding rule
  * open; this one keeps every finite value finite. Rows, positions, the page table, fail-closed
- * behaviour and status are exactly as for gattn_kv_append. Served for head_dim 256 with separate
- * K and V (layer->kv_shared 0; v_new and v_pool required); other layers return
- * GATTN_ERR_UNSUPPORTED, a scale that is not positive and finite GATTN_ERR_BAD_SHAPE.
+ * behaviour and status are exactly as for gattn_kv_append (with layer->kv_shared only K is
+ * written: v_new NULL, v_pool NULL or k_pool, v_scale ignored). Served for the layers
+ * gattn_decode_fp8kv serves; others return GATTN_ERR_UNSUPPORTED, a scale that is not positive
+ * and finite GATTN_ERR_BAD_SHAPE.
  */
 int gattn_kv_append_fp8(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint8_t *k_pool,
                         uint8_t *v_pool, float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table,

@@ -210,7 +210,13 @@ def test_decode_fp8kv_rejects_bad_arguments():
     for bad in (0.0, -1.0, math.inf, math.nan):
         assert st(lay, **dict(ok, k_scale=bad)) == nat.ERR_BAD_SHAPE, bad
         assert st(lay, **dict(ok, v_scale=bad)) == nat.ERR_BAD_SHAPE, bad
-    assert st(g.make_layer("global", 32, 4, 512), **ok) == nat.ERR_UNSUPPORTED
+    assert st(g.make_layer("global", 32, 4, 512), **ok) == 0
+    shared = g.make_layer("global", 32, 4, 512, kv_shared=True)
+    assert st(shared, **dict(ok, v_pool=None)) == 0
+    assert st(shared, **dict(ok, v_pool=2)) == 0                        # v_pool == k_pool
+    assert st(shared, **dict(ok, v_pool=3)) == nat.ERR_BAD_SHAPE
+    assert st(shared, **dict(ok, v_pool=None, v_scale=math.nan)) == 0   # V uses k_scale
+    assert st(g.make_layer("global", 32, 4, 128), **ok) == nat.ERR_UNSUPPORTED
     assert st(g.make_layer("local", 32, 16, 256, window=1024, kv_shared=True), **ok) == nat.ERR_UNSUPPORTED
     assert st(lay, **dict(ok, split_tokens=24)) == nat.ERR_BAD_SPLIT
     assert st(lay, **dict(ok, batch=2)) == nat.ERR_WORKSPACE_TOO_SMALL  # several splits need the workspace
@@ -235,7 +241,11 @@ def test_kv_append_fp8_rejects_bad_arguments():
     for bad in (0.0, -2.0, math.inf, math.nan):
         assert st(lay, **dict(ok, k_scale=bad)) == nat.ERR_BAD_SHAPE, bad
         assert st(lay, **dict(ok, v_scale=bad)) == nat.ERR_BAD_SHAPE, bad
-    assert st(g.make_layer("global", 32, 4, 512), **ok) == nat.ERR_UNSUPPORTED
+    assert st(g.make_layer("global", 32, 4, 512), **ok) == 0
+    shared = g.make_layer("global", 32, 4, 512, kv_shared=True)
+    assert st(shared, **dict(ok, v_new=None, v_pool=None, v_scale=0.0)) == 0
+    assert st(shared, **dict(ok, v_new=2, v_pool=None)) == nat.ERR_BAD_SHAPE
+    assert st(g.make_layer("global", 32, 4, 128), **ok) == nat.ERR_UNSUPPORTED
     assert st(g.make_layer("local", 32, 16, 256, window=1024, kv_shared=True), **ok) == nat.ERR_UNSUPPORTED
     assert st(lay, **dict(ok, batch=-1)) == nat.ERR_BAD_SHAPE
     assert st(lay, **dict(ok, num_pages=0)) == nat.ERR_BAD_SHAPE

@@ -271,3 +271,27 @@ def test_append_and_prefill_past_4_gib(devio):
     assert np.max(np.abs(out - ref_o)) <= 1e-2 and np.max(np.abs(lse - ref_l)) <= 1e-3
     del d, low
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "kv-shared"])
+def test_kv_append_fp8_global_bitwise(devio, spec):
+    """E4M3 append at head_dim 512 (with K = V only the K pool is written): bytes equal the oracle's."""
+    import torch
+    b, L, n_new, cu, k_new, v_new = _case(spec, (48, int(spec.kv_shared)))
+    g = np.random.default_rng(48)
+    k8 = g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    v8 = None if spec.kv_shared else g.integers(0, 256, size=b.k_pool.shape, dtype=np.uint8)
+    ks, vs = workloads.FP8_K_SCALE, workloads.FP8_V_SCALE
+    kp = torch.from_numpy(k8).to("cuda")
+    vp = None if v8 is None else torch.from_numpy(v8).to("cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    devio.nat.gattn_kv_append_fp8(devio.layer_of(spec), devio.dev(k_new), None if v_new is None else devio.dev(v_new),
+                                  kp, vp, ks, vs, b.num_pages, devio.dev(b.page_table.astype(np.int32)), b.pt_stride,
+                                  devio.dev(cu), devio.dev(L), b.B, int(n_new.max()), status)
+    torch.cuda.synchronize()
+    ref_k, ref_v, skipped = oracle.kv_append_fp8(spec.num_kv_heads, spec.head_dim, spec.page_size, cu, L, b.page_table,
+                                                 b.num_pages, k_new, v_new, ks, vs, k8, v8)
+    assert skipped == 0 and int(status.item()) == 0
+    assert np.array_equal(kp.cpu().numpy(), ref_k)
+    if vp is not None:
+        assert np.array_equal(vp.cpu().numpy(), ref_v)

@@ -182,3 +182,27 @@ def test_decode_page_ids_past_4_gib(devio, fp8):
     check(oracle.attend_batch(b), out, lse, f"{'fp8' if fp8 else 'bf16'} pages past 4 GiB")
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("spec,split", [(workloads.GLOBAL_31B, 512), (workloads.GLOBAL_31B, 0),
+                                        (workloads.GLOBAL_31B_KV_SHARED, 1024), (workloads.GLOBAL_31B_KV_SHARED, 512),
+                                        (workloads.GLOBAL_12B, 512)],
+                         ids=["global-512", "global-unsplit", "kv-shared-1024", "kv-shared-512", "12b-global"])
+def test_fp8_global_decode(devio, spec, split):
+    """The global family over E4M3 pools (head_dim 512; with K = V the V side is the K codes with
+    the K scale): ragged rows from 1 token across split edges, poisoned slots."""
+    L = workloads.ragged((82, spec.num_kv_heads, int(spec.kv_shared)), 1, 6000, 8)
+    L[:4] = [1, 16, 1024, 1025]
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (82, int(spec.kv_shared)), back="visible",
+                             poison=True)
+    workloads.with_fp8_kv(b)
+    out, lse = devio.decode_fp8(b, split)
+    check(oracle.attend_batch(b), out, lse, f"fp8 {spec.num_kv_heads}-head global K=V={spec.kv_shared} split {split}")
+
+
+def test_fp8_global_decode_full_batch(devio):
+    """The 32-row global decode workload (contexts ~U{1..8192}, split 512) over E4M3 pools."""
+    b = workloads.cfg2_global_decode()
+    workloads.with_fp8_kv(b)
+    out, lse = devio.decode_fp8(b, 512)
+    check(oracle.attend_batch(b), out, lse, "fp8 global decode B=32")

@@ -190,7 +190,7 @@ class Fp8Kv:
     k: np.ndarray               # uint8, shaped like Batch.k
     v: np.ndarray               # uint8, shaped like Batch.v
     k_pool: np.ndarray          # uint8 [num_pages][Hkv][P][hd]
-    v_pool: np.ndarray
+    v_pool: Optional[np.ndarray]  # None with K = V
     k_scale: float
     v_scale: float
 
@@ -212,10 +212,15 @@ def e4m3_codes(bf16_bits: np.ndarray, scale: float) -> np.ndarray:
 
 def with_fp8_kv(b: Batch, k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE) -> Batch:
     """Attach an E4M3 copy of the batch's K/V (contiguous rows and pools, element by element, so
-    the two sides hold the same codes). Needs separate K and V."""
-    assert b.v is not None and b.v_pool is not None
-    b.fp8 = Fp8Kv(e4m3_codes(b.k, k_scale), e4m3_codes(b.v, v_scale), e4m3_codes(b.k_pool, k_scale),
-                  e4m3_codes(b.v_pool, v_scale), float(k_scale), float(v_scale))
+    the two sides hold the same codes). With K = V the V side is the K codes with the K scale and
+    there is no V pool."""
+    k8 = e4m3_codes(b.k, k_scale)
+    kp8 = e4m3_codes(b.k_pool, k_scale)
+    if b.v is None:
+        b.fp8 = Fp8Kv(k8, k8, kp8, None, float(k_scale), float(k_scale))
+    else:
+        b.fp8 = Fp8Kv(k8, e4m3_codes(b.v, v_scale), kp8, e4m3_codes(b.v_pool, v_scale), float(k_scale),
+                      float(v_scale))
     return b
 
 
