@@ -257,6 +257,30 @@ def local_decode_measure(torch, devio, workloads, traffic, stream, flush, steps=
     return out
 
 
+def global_fp8_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
+    """The measured global decode batch (32 rows, contexts ~U{1..8192}, split 512) over E4M3 pools,
+    pools filled on the device; GB/s of FP8 bytes and the speed-up over the same rows in bf16."""
+    L = workloads.ragged((2, 0), 1, 8192, 32)
+    lay = workloads.paged_layout(workloads.GLOBAL_31B, L, (2, 0))
+    s = lay.spec
+    out = {}
+    for name, fp8 in (("bf16", None), ("fp8", (workloads.FP8_K_SCALE, workloads.FP8_V_SCALE))):
+        if fp8 is None:
+            d = devio.DeviceLayout(lay, workloads.fill_normal_bf16_device)
+        else:
+            d = devio.DeviceLayout(lay, workloads.fill_e4m3_device, fp8=fp8)
+        kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, L,
+                                     2 if fp8 is None else 1)
+        for _ in range(5):
+            d.decode(512)
+        t = median(event_times(torch, stream, lambda: d.decode(512), steps))
+        out[name] = {"kv_bytes": kv, "us": round(t * 1e6, 2), "gbs": round(kv / t / 1e9, 1)}
+        del d
+    out["speedup"] = round(out["bf16"]["us"] / out["fp8"]["us"], 3)
+    out["workload"] = "global decode: batch 32, hd 512, 4 KV heads, contexts ~U{1..8192}, split 512; bf16 vs E4M3 pools"
+    return out
+
+
 def gemma12b_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
     """The 12B geometry: global decode (batch 32, 16 q heads over one KV head, hd 512, contexts
     ~U{1..8192}, split 512) as KV GB/s, and the 12B mixed step's prefill rows of both families as
@@ -355,6 +379,7 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
         out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
         out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
     # the same sweep with the 50 local layers' K/V in FP8 (E4M3) pools (gattn_decode_fp8kv): half their bytes
+    layers8 = None
     try:
         layers8 = []
         for (fam, d), lay in zip(layers, lays):
@@ -372,10 +397,23 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
         kv8 = kv_fam["global"] + kv_fam["local"] // 2
         out["fp8_local"] = {"kv_bytes": kv8, "ms": round(t8 * 1e3, 4), "gbs": round(kv8 / t8 / 1e9, 1),
                             "speedup_vs_bf16": round(t / t8, 3)}
-        del layers8
+        # every layer in FP8: the global layers' K=V pools too (their one scale serves K and V)
+        del layers
+        layers = []
+        for (fam, d), lay in zip(layers8, lays):
+            if fam == "global":
+                d = devio.DeviceLayout(lay, workloads.fill_e4m3_device, workspace=ws,
+                                       fp8=(workloads.FP8_K_SCALE, workloads.FP8_K_SCALE))
+            layers.append((fam, d))
+        layers8 = layers
+        sweep8()
+        torch.cuda.synchronize()
+        ta = median(event_times(torch, stream, sweep8, reps))
+        out["fp8_all"] = {"kv_bytes": kv_total // 2, "ms": round(ta * 1e3, 4),
+                          "gbs": round(kv_total // 2 / ta / 1e9, 1), "speedup_vs_bf16": round(t / ta, 3)}
     except Exception as e:  # report, never hide
-        out["fp8_local"] = {"error": str(e)[:200]}
-    del layers, ws
+        out["fp8_error"] = str(e)[:200]
+    layers = layers8 = ws = None
     torch.cuda.empty_cache()
 
     lay = workloads.long_global_decode(rows=())
@@ -506,6 +544,10 @@ def main():
             result["sweep"], result["long_decode"] = sweep_measure(torch, devio, workloads, traffic, stream, flush)
         except Exception as e:  # report, never hide
             result["sweep"] = {"error": str(e)[:300]}
+        try:
+            result["global_decode_fp8"] = global_fp8_measure(torch, devio, workloads, traffic, stream, flush)
+        except Exception as e:  # report, never hide
+            result["global_decode_fp8"] = {"error": str(e)[:300]}
         try:
             result["gemma12b"] = gemma12b_measure(torch, devio, workloads, traffic, stream, flush)
         except Exception as e:  # report, never hide
