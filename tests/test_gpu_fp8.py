@@ -1,7 +1,9 @@
 """Decode over an FP8 (E4M3) KV pool on the GPU against the fp64 oracle over the dequantized
 K/V (O max-abs 1e-2, LSE max-abs 1e-3): local rows at window edges and across many windows,
-every split policy, the 12B local geometry, a head_dim 256 global layer, the full local decode
-batch, poisoned never-visible slots and fail-closed rows."""
+every split policy, the 12B local geometry, a head_dim 256 global layer, the global family at
+head_dim 512 with and without K = V (and its single-KV-head 12B layer), the full local and global
+decode batches, poisoned never-visible slots, fail-closed rows, a graph replay, and pools whose
+pages sit past byte offset 2^32."""
 import numpy as np
 import pytest
 
