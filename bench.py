@@ -149,7 +149,7 @@ def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
                     "decode_rows_us": round(td * 1e6, 2), "decode_rows_kv_bytes": kv,
                     "decode_rows_gbs": round(kv / td / 1e9, 1),
                     "step_ms": round(tstep * 1e3, 4), "single_launch_step_ms": round(tone * 1e3, 4),
-                    "workload": f"{fam}: 4 chunks x 2048 queries, priors {pre.ctx_lens.tolist()}; "
+                    "workload": f"{fam}: 4 chunks x 2048 queries, priors {(pre.ctx_lens - pre.q_lens).tolist()}; "
                                 f"60 decode rows, contexts ~U{{1..8192}}, split 512"}
         del d, dd
     return out
@@ -305,7 +305,7 @@ def gemma12b_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
             dp.prefill()
         tp = median(event_times(torch, stream, dp.prefill, 10, flush))
         out[f"{fam}_prefill"] = {"workload": f"12B {fam} prefill: 4 chunks x 2048 queries, priors "
-                                             f"{pre.ctx_lens.tolist()}", "flops": flops, "ms": round(tp * 1e3, 4),
+                                             f"{(pre.ctx_lens - pre.q_lens).tolist()}", "flops": flops, "ms": round(tp * 1e3, 4),
                                  "tflops": round(flops / tp / 1e12, 2),
                                  "frac_of_bf16_peak": round(flops / tp / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         del dp

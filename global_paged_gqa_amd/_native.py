@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgattn.so")
+# GATTN_LIBRARY names another build of the library to load (the CPU sanitizer tests load a host-only
+# build whose kernel launches all fail); by default the in-tree gfx950 build.
+LIB_PATH = os.environ.get("GATTN_LIBRARY") or os.path.join(_HERE, "libgattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the gfx950 library first "

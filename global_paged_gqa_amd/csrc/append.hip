@@ -60,6 +60,14 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     if (i0 >= n)
         return;
     const int L = a.ctx_lens[r];
+    // A malformed row (more new tokens than cached ones, or than the max_new bound the grid was
+    // sized by, which would leave tokens past the grid unwritten) fails closed as a whole: none
+    // of its tokens is written and the row's first workgroup raises the status flag.
+    if (n > L || n > a.max_new) {
+        if (blockIdx.x == 0 && threadIdx.x == 0 && a.status)
+            atomicOr(a.status, 1);
+        return;
+    }
     const int nt = min(kTok, n - i0);
     const int Hkv = a.num_kv_heads;
     const int rows = nt * Hkv;
@@ -77,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
                 continue;
             const int it = row / Hkv, kvh = row - it * Hkv;
             const int t = L - n + i0 + it;  // absolute position of the token
-            const int pid = (L >= n && (t >> 4) < a.pt_stride) ? pt[t >> 4] : -1;
+            const int pid = (t >> 4) < a.pt_stride ? pt[t >> 4] : -1;
             if (pid < 0 || pid >= a.num_pages) {
                 bad = 1;
                 continue;

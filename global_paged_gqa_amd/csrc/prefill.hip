@@ -269,6 +269,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int tile_q = qt * BQ;        // first query of the tile (within the row)
     if (q_len <= 0 || tile_q >= q_len)
         return;
+    // A row with more queries than max_q (the bound the grid was sized by) would leave the
+    // queries past the last tile unwritten: the row fails closed, each of its tiles writing NaN
+    // over every gridDim.x-th block of BQ queries, so that all of them are covered.
+    if (q_len > a.max_q) {
+        const float qnan = __builtin_nanf("");
+        const uint32_t nan2 = pack_bf16x2(qnan, qnan);
+        for (int i0 = tile_q; i0 < q_len; i0 += gridDim.x * BQ)
+            for (int e = threadIdx.x; e < min(BQ, q_len - i0) * g; e += kThreads) {
+                const int64_t orow = (int64_t)(q0 + i0 + e / g) * Hq + kvh * g + e % g;
+                a.lse[orow] = qnan;
+                for (int d = 0; d < HD; d += 8)
+                    *(u32x4 *)(a.out + orow * HD + d) = u32x4{nan2, nan2, nan2, nan2};
+            }
+        return;
+    }
     const int nq = min(BQ, q_len - tile_q);
     const int p_first = L - q_len + tile_q;  // absolute position of the tile's first query
     const int p_last = p_first + nq - 1;

@@ -197,6 +197,12 @@ int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_
  *   max_q      host-side upper bound of every row's q_len (sets the grid).
  *   out        [total_q][num_q_heads][head_dim] bf16.
  *   lse        [total_q][num_q_heads] fp32, natural log.
+ * Fail closed on device-side data (pegainfer "[Model] Gemma 4 M3 31B", Proposed
+ * Plan: what is not served fails closed): a row whose q_len exceeds max_q or
+ * ctx_lens[r], or whose context runs past the page table, gets NaN O and LSE for
+ * every one of its queries; a page id outside [0, num_pages) in a page that a
+ * block of 128 query rows reads turns that block's outputs NaN. Nothing is read
+ * or written outside the row's own queries and the pool.
  */
 int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
                   const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
@@ -204,7 +210,11 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
                   float *lse, void *stream);
 
 /*
- * Logsumexp merge of split partials (the combine half of split-KV decoding).
+ * Logsumexp merge of split partials: the combine half of split-KV decoding
+ * (pegainfer "[Model] Gemma 4 M3 31B", Proposed Plan: the split-KV chunk policy;
+ * Core AI card, "--metal-sdpa" section: a flash-decode kernel with a split
+ * factor), exported so that partials produced elsewhere (another split schedule,
+ * or other devices' shares of one long context) merge the same way.
  * For each (row, head): M = max over splits of lse_s; LSE = M + ln sum_s
  * exp(lse_s - M); O = sum_s exp(lse_s - LSE) o_s. Splits with lse_s = -inf are
  * empty and are skipped (their o_s is never read). A row whose splits are all
@@ -239,10 +249,11 @@ int gattn_combine(int batch, int num_q_heads, int head_dim, int num_splits, cons
  *   cu_new     [batch + 1] int32 (device memory), cu_new[0] = 0, nondecreasing.
  *   ctx_lens   [batch] int32 (device memory), ctx_lens[r] >= n_r.
  *   max_new    host-side upper bound of every n_r (sets the grid).
- *   status     optional int32 (device memory, may be NULL). Fail closed: a token
- *              whose position lies beyond the page table, whose page id is
- *              outside [0, num_pages), or whose row has ctx_lens[r] < n_r is not
- *              written, and the kernel ORs 1 into *status. The caller clears it.
+ *   status     optional int32 (device memory, may be NULL). Fail closed: a row
+ *              with n_r > ctx_lens[r] or n_r > max_new writes none of its
+ *              tokens, a token whose position lies beyond the page table or
+ *              whose page id is outside [0, num_pages) is not written, and in
+ *              either case the kernel ORs 1 into *status. The caller clears it.
  * Rows with n_r = 0 are skipped. Enqueues one kernel on `stream`.
  */
 int gattn_kv_append(const gattn_layer *layer, const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool,

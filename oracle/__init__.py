@@ -21,6 +21,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _HDR = os.path.join(_HERE, "oracle.h")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt oracle library to load instead of building liboracle.so (the sanitizer tests point this
+# at an AddressSanitizer / UndefinedBehaviorSanitizer build of the same oracle.c).
+_LIB_OVERRIDE = os.environ.get("GATTN_ORACLE_LIB")
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 _lock = threading.Lock()
 _lib = None
 
@@ -39,12 +44,23 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into ``path`` (loaded
+    through GATTN_ORACLE_LIB by a process that preloads the sanitizer runtime)."""
+    subprocess.check_call(["gcc", *SANITIZE_FLAGS, "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", path, _SRC,
+                           "-lm"])
+    return path
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            if _LIB_OVERRIDE:
+                lib = ctypes.CDLL(_LIB_OVERRIDE)
+            else:
+                build()
+                lib = ctypes.CDLL(_LIB)
             i32p = ctypes.POINTER(ctypes.c_int32)
             u16p = ctypes.POINTER(ctypes.c_uint16)
             f64p = ctypes.POINTER(ctypes.c_double)
@@ -63,7 +79,7 @@ def _load():
             lib.oracle_threads.argtypes = []
             lib.oracle_kv_append.restype = ctypes.c_int64
             lib.oracle_kv_append.argtypes = [c_int, c_int, c_int, c_int, i32p, i32p, i32p, c_int, ctypes.c_int64,
-                                             u16p, u16p, u16p, u16p]
+                                             c_int, u16p, u16p, u16p, u16p]
             u8p = ctypes.POINTER(ctypes.c_uint8)
             lib.oracle_attend_fp8kv.restype = c_int
             lib.oracle_attend_fp8kv.argtypes = [c_int, c_int, c_int, c_int, c_int, c_double, c_int,
@@ -76,7 +92,7 @@ def _load():
             lib.oracle_e4m3_encode_n.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_float), u8p]
             lib.oracle_kv_append_fp8.restype = ctypes.c_int64
             lib.oracle_kv_append_fp8.argtypes = [c_int, c_int, c_int, c_int, i32p, i32p, i32p, c_int, ctypes.c_int64,
-                                                 u16p, u16p, ctypes.c_float, ctypes.c_float, u8p, u8p]
+                                                 c_int, u16p, u16p, ctypes.c_float, ctypes.c_float, u8p, u8p]
             _lib = lib
     return _lib
 
@@ -154,9 +170,10 @@ def merge(lse_parts, o_parts):
 
 
 def kv_append(num_kv_heads: int, head_dim: int, page_size: int, cu_new, ctx_lens, page_table, num_pages: int,
-              k_new, v_new, k_pool, v_pool):
+              k_new, v_new, k_pool, v_pool, max_new=None):
     """Paged KV append (``oracle_kv_append``): returns (k_pool', v_pool', skipped tokens) with the
-    new tokens copied into copies of the given pools."""
+    new tokens copied into copies of the given pools. ``max_new`` is the call's declared bound on a
+    row's new tokens (None: no bound); a row above it writes nothing."""
     lib = _load()
     cu_new, ctx_lens = _i32(cu_new), _i32(ctx_lens)
     pt = _i32(page_table)
@@ -167,8 +184,8 @@ def kv_append(num_kv_heads: int, head_dim: int, page_size: int, cu_new, ctx_lens
     B = int(ctx_lens.shape[0])
     n = lib.oracle_kv_append(num_kv_heads, head_dim, page_size, B, _ptr(cu_new, ctypes.c_int32),
                              _ptr(ctx_lens, ctypes.c_int32), _ptr(pt, ctypes.c_int32), int(pt.shape[1]),
-                             int(num_pages), _ptr(k_new, ctypes.c_uint16), _ptr(v_new, ctypes.c_uint16),
-                             _ptr(kp, ctypes.c_uint16), _ptr(vp, ctypes.c_uint16))
+                             int(num_pages), -1 if max_new is None else int(max_new), _ptr(k_new, ctypes.c_uint16),
+                             _ptr(v_new, ctypes.c_uint16), _ptr(kp, ctypes.c_uint16), _ptr(vp, ctypes.c_uint16))
     if n < 0:
         raise OracleError(f"oracle_kv_append failed: {n}")
     return kp, vp, int(n)
@@ -215,7 +232,7 @@ def e4m3_encode(x):
 
 
 def kv_append_fp8(num_kv_heads: int, head_dim: int, page_size: int, cu_new, ctx_lens, page_table, num_pages: int,
-                  k_new, v_new, k_scale: float, v_scale: float, k_pool8, v_pool8):
+                  k_new, v_new, k_scale: float, v_scale: float, k_pool8, v_pool8, max_new=None):
     """``kv_append`` into E4M3 pools (``oracle_kv_append_fp8``): returns (k_pool', v_pool', skipped)."""
     lib = _load()
     cu_new, ctx_lens = _i32(cu_new), _i32(ctx_lens)
@@ -227,8 +244,9 @@ def kv_append_fp8(num_kv_heads: int, head_dim: int, page_size: int, cu_new, ctx_
     B = int(ctx_lens.shape[0])
     n = lib.oracle_kv_append_fp8(num_kv_heads, head_dim, page_size, B, _ptr(cu_new, ctypes.c_int32),
                                  _ptr(ctx_lens, ctypes.c_int32), _ptr(pt, ctypes.c_int32), int(pt.shape[1]),
-                                 int(num_pages), _ptr(k_new, ctypes.c_uint16), _ptr(v_new, ctypes.c_uint16),
-                                 float(k_scale), float(v_scale), _ptr(kp, ctypes.c_uint8), _ptr(vp, ctypes.c_uint8))
+                                 int(num_pages), -1 if max_new is None else int(max_new),
+                                 _ptr(k_new, ctypes.c_uint16), _ptr(v_new, ctypes.c_uint16), float(k_scale),
+                                 float(v_scale), _ptr(kp, ctypes.c_uint8), _ptr(vp, ctypes.c_uint8))
     if n < 0:
         raise OracleError(f"oracle_kv_append_fp8 failed: {n}")
     return kp, vp, int(n)

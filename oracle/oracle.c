@@ -447,14 +447,16 @@ typedef struct {
 } append_dst;
 
 static int64_t append_rows(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                           const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                           const uint16_t *v_new, const append_dst *dst_pools)
+                           const int32_t *page_table, int pt_stride, int64_t num_pages, int max_new,
+                           const uint16_t *k_new, const uint16_t *v_new, const append_dst *dst_pools)
 {
     const int fp8 = dst_pools->k_pool8 != NULL;
     int64_t skipped = 0;
     for (int r = 0; r < B; ++r) {
         const int64_t n = (int64_t)cu_new[r + 1] - cu_new[r];
-        if ((int64_t)ctx_lens[r] < n) { /* more new tokens than the cache holds: the row is malformed */
+        /* A malformed row fails closed as a whole: more new tokens than the cache holds, or more
+         * than the call's declared bound max_new (when max_new >= 0). */
+        if ((int64_t)ctx_lens[r] < n || (max_new >= 0 && n > max_new)) {
             skipped += n;
             continue;
         }
@@ -493,24 +495,27 @@ static int64_t append_rows(int Hkv, int hd, int page_size, int B, const int32_t 
 }
 
 int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool)
+                         const int32_t *page_table, int pt_stride, int64_t num_pages, int max_new,
+                         const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool)
 {
     if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
         !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool))
         return ORACLE_BAD_ARG;
     const append_dst d = {k_pool, v_pool, NULL, NULL, 1.0f, 1.0f};
-    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, k_new, v_new, &d);
+    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, max_new, k_new,
+                       v_new, &d);
 }
 
 int64_t oracle_kv_append_fp8(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                             const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                             const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool, uint8_t *v_pool)
+                             const int32_t *page_table, int pt_stride, int64_t num_pages, int max_new,
+                             const uint16_t *k_new, const uint16_t *v_new, float k_scale, float v_scale,
+                             uint8_t *k_pool, uint8_t *v_pool)
 {
     if (Hkv <= 0 || hd <= 0 || page_size <= 0 || B < 0 || pt_stride <= 0 || num_pages <= 0 || !cu_new ||
         !ctx_lens || !page_table || !k_new || !k_pool || (v_new && !v_pool) || !(k_scale > 0.0f) ||
         !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
         return ORACLE_BAD_ARG;
     const append_dst d = {NULL, NULL, k_pool, v_pool, k_scale, v_scale};
-    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, k_new, v_new, &d);
+    return append_rows(Hkv, hd, page_size, B, cu_new, ctx_lens, page_table, pt_stride, num_pages, max_new, k_new,
+                       v_new, &d);
 }

@@ -50,11 +50,12 @@ int oracle_layer_is_global(int layer, int n_layers);
  * page_table[r][t / page_size], slot t % page_size, as pool[page][kv_head][slot][head_dim]. For
  * every such token whose position fits the table and whose page id is in [0, num_pages), copies
  * its [Hkv][hd] K row (and V row when v_new is not NULL) into the pools; all other pool values
- * stay. A row with ctx_lens[r] < n_r is malformed and writes nothing. Returns the number of tokens
+ * stay. A row with ctx_lens[r] < n_r, or with n_r > max_new when max_new >= 0 (the call's declared
+ * bound on n_r), is malformed and writes nothing (fail closed). Returns the number of tokens
  * skipped (malformed row, position beyond the table, page id out of range), or ORACLE_BAD_ARG. */
 int64_t oracle_kv_append(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                         const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                         const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool);
+                         const int32_t *page_table, int pt_stride, int64_t num_pages, int max_new,
+                         const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_pool, uint16_t *v_pool);
 
 /* FP8 KV pool: K and V hold OCP E4M3 codes (one byte per element, same [token][Hkv][hd] layout as
  * above) standing for code_value * k_scale and code_value * v_scale (one scale per tensor, both
@@ -76,8 +77,9 @@ void oracle_e4m3_encode_n(int64_t n, const float *x, uint8_t *out);
  * quotient bf16_value / scale (k_scale for K, v_scale for V); a NaN value stores NaN with its own
  * sign bit. */
 int64_t oracle_kv_append_fp8(int Hkv, int hd, int page_size, int B, const int32_t *cu_new, const int32_t *ctx_lens,
-                             const int32_t *page_table, int pt_stride, int64_t num_pages, const uint16_t *k_new,
-                             const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool, uint8_t *v_pool);
+                             const int32_t *page_table, int pt_stride, int64_t num_pages, int max_new,
+                             const uint16_t *k_new, const uint16_t *v_new, float k_scale, float v_scale,
+                             uint8_t *k_pool, uint8_t *v_pool);
 
 /* OpenMP threads the oracle runs with. */
 int oracle_threads(void);

@@ -1,0 +1,17 @@
+// Launch stubs for a host-only build of the library's C ABI (csrc/gattn.cpp), used by the CPU
+// sanitizer tests: argument validation, split planning and workspace sizing run for real under
+// AddressSanitizer and UndefinedBehaviorSanitizer, while every kernel launch fails with
+// hipErrorInvalidValue (reported as GATTN_ERR_HIP), so this build can never compute a result.
+#include "kernels.h"
+
+namespace gattn {
+
+hipError_t launch_kv_append(const AppendArgs &, int, int, bool, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_split(const DecodeArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_split_fp8(const DecodeArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_combine(int, int, int, int, const float *, const float *, uint16_t *, float *, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+hipError_t launch_prefill(const PrefillArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
+
+}  // namespace gattn

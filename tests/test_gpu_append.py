@@ -44,7 +44,7 @@ def _case(spec, key, B=7, max_len=5000):
     return b, L, n_new, cu, k_new, v_new
 
 
-def _run(devio, spec, b, L, n_new, cu, k_new, v_new, page_table=None):
+def _run(devio, spec, b, L, n_new, cu, k_new, v_new, page_table=None, max_new=None):
     import torch
     nat = devio.nat
     lay = devio.layer_of(spec)
@@ -54,7 +54,7 @@ def _run(devio, spec, b, L, n_new, cu, k_new, v_new, page_table=None):
     pt = b.page_table if page_table is None else page_table
     nat.gattn_kv_append(lay, devio.dev(k_new), None if v_new is None else devio.dev(v_new), kp, vp, b.num_pages,
                         devio.dev(pt.astype(np.int32)), pt.shape[1], devio.dev(cu), devio.dev(L), b.B,
-                        int(n_new.max()), status)
+                        int(n_new.max()) if max_new is None else int(max_new), status)
     torch.cuda.synchronize()
     kp_h = kp.cpu().numpy().view(np.uint16)
     vp_h = None if vp is None else vp.cpu().numpy().view(np.uint16)
@@ -88,6 +88,22 @@ def test_kv_append_fails_closed(devio):
     ref_k, ref_v, skipped = oracle.kv_append(spec.num_kv_heads, spec.head_dim, spec.page_size, cu, L_bad, pt,
                                              b.num_pages, k_new, v_new, b.k_pool, b.v_pool)
     assert skipped > 0 and status == 1
+    assert np.array_equal(kp, ref_k) and np.array_equal(vp, ref_v)
+
+
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.LOCAL_31B], ids=["global", "local"])
+def test_kv_append_row_above_max_new_fails_closed(devio, spec):
+    """max_new (the host bound that sizes the grid) below one row's count of new tokens: that row
+    (2048 new tokens against the largest count of the others, 300 or less) writes none of them and
+    raises the status flag, where a fail-open kernel would write the tokens its grid covers and
+    silently drop the rest; every other row is written as usual."""
+    b, L, n_new, cu, k_new, v_new = _case(spec, (44, spec.num_kv_heads))
+    mx = int(n_new[1:].max())
+    assert n_new[0] == 2048 and 0 < mx < 2048
+    kp, vp, status = _run(devio, spec, b, L, n_new, cu, k_new, v_new, max_new=mx)
+    ref_k, ref_v, skipped = oracle.kv_append(spec.num_kv_heads, spec.head_dim, spec.page_size, cu, L, b.page_table,
+                                             b.num_pages, k_new, v_new, b.k_pool, b.v_pool, max_new=mx)
+    assert skipped == 2048 and status == 1
     assert np.array_equal(kp, ref_k) and np.array_equal(vp, ref_v)
 
 

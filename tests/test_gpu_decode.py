@@ -260,3 +260,94 @@ def test_combine_matches_fp64_merge(devio):
     assert np.array_equal(fin, np.isfinite(got_l))
     assert np.max(np.abs(got_l[fin] - ref_l[fin])) < 1e-5
     assert np.max(np.abs(got_o - ref_o)) < 1e-2
+
+
+# ------------------------------------------------------------------------ head_dim 512 index probes
+PROBE_L = 3000
+PROBE_T = (0, 1, 15, 16, 511, 512, 1023, 1024, 1025, 2047, 2048, 2559, 2560, PROBE_L - 17, PROBE_L - 16,
+           PROBE_L - 1)
+
+
+def _probe_batch(spec, t_star, key, n_filler=0, pt_stride=None, code_of=None):
+    """Row 0 (L = PROBE_L): every query head is e_0, K[t*] = 200 e_0 and every other key 0, so at
+    scale 1 every other weight underflows to exactly 0 and O must be V[t*] bit for bit. V[t*]
+    holds a code of t* and the head dim (with K=V, V[t*] is K[t*]: the code sits in dims 1..hd-1
+    beside the 200). Rows 1..n_filler are short random rows that only enlarge the grid."""
+    L = [PROBE_L] + [1 + 7 * i for i in range(n_filler)]
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), key, back="all", pt_stride=pt_stride)
+    hd, P = spec.head_dim, spec.page_size
+    b.q[0] = 0
+    b.q[0, :, 0] = workloads.f32_to_bf16_bits(np.float32([1.0]))[0]
+    code = workloads.f32_to_bf16_bits(np.float32(np.arange(hd) + 0.5 + (t_star % 97)))
+    kk = np.zeros((PROBE_L, spec.num_kv_heads, hd), np.uint16)
+    if spec.kv_shared:
+        kk[t_star, :, :] = code
+    kk[t_star, :, 0] = workloads.f32_to_bf16_bits(np.float32([200.0]))[0]
+    pt = b.page_table[0]
+    for t in range(PROBE_L):
+        b.k_pool[pt[t // P], :, t % P, :] = kk[t]
+        if not spec.kv_shared:
+            b.v_pool[pt[t // P], :, t % P, :] = code if t == t_star else b.v_pool[pt[t // P], :, t % P, :]
+    want = kk[t_star, 0] if spec.kv_shared else code
+    return b, workloads.bf16_bits_to_f32(want).astype(np.float64)
+
+
+HD512_SHAPES = {  # name: (kv_shared, split, filler rows, max_ctx, pt_stride) -> items = slots * 4 * rows
+    "global-4waves-32k": (False, 512, 0, None, None),        # 6 x 4 = 24 items
+    "global-4waves-16k": (False, 512, 1, 20000, 1250),       # 40 x 4 x 2 = 320 items
+    "global-1wave": (False, 512, 8, 8192, None),              # 16 x 4 x 9 = 576 items
+    "kv-shared-4waves-32k": (True, 1024, 0, None, None),     # 3 x 4 = 12 items
+    "kv-shared-4waves-16k": (True, 1024, 1, 40000, 2500),    # 40 x 4 x 2 = 320 items
+    "kv-shared-1wave": (True, 1024, 8, 16384, None),         # 16 x 4 x 9 = 576 items
+}
+
+
+@pytest.mark.parametrize("shape", list(HD512_SHAPES))
+def test_position_probe_hd512(devio, shape):
+    """The position probe at head_dim 512 in each launch shape of the global family (one wave per
+    item, or four head-dim waves with 32 KB or 16 KB slices; separate pools and K=V), swept over
+    page, split and shape-relevant edges: the output must be V[t*] bit for bit in every head."""
+    shared, split, n_fill, max_ctx, pt_stride = HD512_SHAPES[shape]
+    spec = workloads.LayerSpec("global", 32, 4, 512, kv_shared=shared, scale=1.0)
+    for t_star in PROBE_T:
+        b, want = _probe_batch(spec, t_star, (15, t_star, int(shared)), n_fill, pt_stride)
+        d = devio.DeviceBatch(b)
+        d.decode(split, max_ctx)
+        out, _ = d.result()
+        for h in range(spec.num_q_heads):
+            assert np.array_equal(out[0, h], want), (shape, t_star, h)
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["separate", "kv-shared"])
+def test_position_probe_hd512_fp8(devio, shared):
+    """The position probe over E4M3 pools at head_dim 512 (scales 1): K[t*] = 192 e_0 (an E4M3
+    value), every other key code 0, and V[t*] (K[t*] with K=V) a code of t* and the dim; the
+    output must be the widened V[t*] bit for bit."""
+    spec = workloads.LayerSpec("global", 32, 4, 512, kv_shared=shared, scale=1.0)
+    split = 1024 if shared else 512
+    e4m3_192 = 0x74    # 1.5 * 2^7: exponent field 14 (bias 7), mantissa 0b100
+    for t_star in PROBE_T:
+        b, _ = _probe_batch(spec, t_star, (16, t_star, int(shared)))
+        hd, P, Hkv = spec.head_dim, spec.page_size, spec.num_kv_heads
+        # codes 0x08..0x57 (2^-6 .. 15, all finite) keyed by t* and the dim
+        vcode = (8 + (np.arange(hd) + 3 * t_star) % 80).astype(np.uint8)
+        k8 = np.zeros((PROBE_L, Hkv, hd), np.uint8)
+        if shared:
+            k8[t_star] = vcode
+        k8[t_star, :, 0] = e4m3_192
+        v8 = None if shared else np.zeros((PROBE_L, Hkv, hd), np.uint8)
+        if not shared:
+            v8[:] = 0x38   # 1.0 everywhere else
+            v8[t_star] = vcode
+        kp8 = np.zeros(b.k_pool.shape, np.uint8)
+        vp8 = None if shared else np.zeros(b.k_pool.shape, np.uint8)
+        pt = b.page_table[0]
+        for t in range(PROBE_L):
+            kp8[pt[t // P], :, t % P, :] = k8[t]
+            if not shared:
+                vp8[pt[t // P], :, t % P, :] = v8[t]
+        b.fp8 = workloads.Fp8Kv(k8, k8 if shared else v8, kp8, vp8, 1.0, 1.0)
+        want = oracle.e4m3_value((k8 if shared else v8)[t_star, 0])
+        out, _ = devio.decode_fp8(b, split)
+        for h in range(spec.num_q_heads):
+            assert np.array_equal(out[0, h], want), (shared, t_star, h)

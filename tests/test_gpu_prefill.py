@@ -92,19 +92,59 @@ def test_prefill_zero_length_rows(devio):
     check(b, out, lse, tag="zero-length row")
 
 
-@pytest.mark.parametrize("family", ["global", "local"])
-def test_cfg4_prefill_sampled(devio, family):
-    """The mixed step's prefill rows at full size (4 x 2048 queries after priors U{0..6144}),
-    checked on sampled queries: chunk edges, tile edges, window edges and random ones."""
-    pre, _ = workloads.cfg4_mixed(family)
-    out, lse = devio.prefill(pre)
+@pytest.fixture(scope="module", params=["global", "local"])
+def cfg4_step(request, devio):
+    """The mixed step at full size (4 prefill rows of 2048 queries after priors U{0..6144}, 60
+    decode rows with contexts U{1..8192}): gattn_prefill then gattn_decode on one stream, the
+    launch pair the benchmark times; results copied back once both have run."""
+    import torch
+    pre, dec = workloads.cfg4_mixed(request.param)
+    dp, dd = devio.DeviceBatch(pre), devio.DeviceBatch(dec)
+    stream = torch.cuda.current_stream()
+    dp.prefill(stream=stream)
+    dd.decode(512, stream=stream)
+    torch.cuda.synchronize()
+    return request.param, pre, dec, dp.result(), dd.result()
+
+
+def test_cfg4_outputs_all_finite(cfg4_step):
+    family, pre, dec, (out, lse), (dout, dlse) = cfg4_step
+    assert out.shape[0] == int(pre.q_lens.sum()) and dout.shape[0] == dec.B
+    for a in (out, lse, dout, dlse):
+        assert np.all(np.isfinite(a)), family
+
+
+def test_cfg4_prefill_full_rows(cfg4_step):
+    """Every query of whole prefill rows against the oracle: all four local rows; for the global
+    family the row with the shortest prior (about 3e11 fp64 flop), the others on sampled queries
+    (chunk, tile and window edges, and random ones)."""
+    family, pre, _, (out, lse), _ = cfg4_step
+    full = list(range(pre.B)) if family == "local" else [int(np.argmin(pre.ctx_lens - pre.q_lens))]
+    for r in full:
+        ref_o, ref_l = oracle.attend_batch(pre, [r])
+        cq = pre.cu_q
+        o, l = out[cq[r]:cq[r + 1]], lse[cq[r]:cq[r + 1]]
+        eo, el = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(l - ref_l)))
+        print(f"cfg4 {family} prefill row {r} (all {cq[r + 1] - cq[r]} queries): max|dO|={eo:.3e} "
+              f"max|dLSE|={el:.3e}", flush=True)
+        assert eo <= TOL_O and el <= TOL_LSE, (r, eo, el)
     rng = np.random.default_rng(3)
     picks = []
     for r in range(pre.B):
+        if r in full:
+            continue
         C = int(pre.q_lens[r])
         fixed = [0, 1, 7, 8, 15, 16, 63, 64, 127, 128, 1023, 1024, C - 2, C - 1]
         picks += [(r, i) for i in sorted(set([i for i in fixed if 0 <= i < C] + list(rng.integers(0, C, 10))))]
-    check(pre, out, lse, picks, tag=f"cfg4 {family} prefill (sampled)")
+    if picks:
+        check(pre, out, lse, picks, tag=f"cfg4 {family} prefill (sampled on the other rows)")
+
+
+def test_cfg4_decode_rows_after_prefill(cfg4_step):
+    """All 60 decode rows of the step, issued after the prefill on the same stream, against the
+    oracle element by element."""
+    family, _, dec, _, (dout, dlse) = cfg4_step
+    check(dec, dout, dlse, tag=f"cfg4 {family} decode rows after the prefill")
 
 
 @pytest.mark.parametrize("family", ["global", "local"])
@@ -222,3 +262,44 @@ def test_mixed_step_single_launch(devio, family):
     mix = workloads.concat_batches(pre, dec)
     out, lse = devio.prefill(mix)
     check(mix, out, lse, tag=f"single-launch mixed {family}")
+
+
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.LOCAL_31B], ids=["global", "local"])
+def test_prefill_fails_closed(devio, spec):
+    """Device-side data the call cannot serve gives NaN O and LSE for the affected rows only, with
+    no read outside the table or the pool: page 0 (seen by every query, contexts < window) out of
+    range (row 1) or -1 (row 3); more queries than cached tokens (row 4); a context past the page
+    table (row 5); more queries than max_q (row 6: 700 queries against max_q 300, so its queries
+    past the grid's last tile are written NaN as well). Rows 0 and 2 match the oracle and are
+    bitwise what a clean call gives them."""
+    import torch
+    L = np.array([700, 400, 650, 300, 500, 450, 900], np.int32)
+    C = np.array([200, 150, 100, 120, 50, 60, 700], np.int32)
+    b = workloads.make_batch(spec, L, C, (36, spec.head_dim), back="visible")
+    d = devio.DeviceBatch(b)
+    d.prefill(max_q=700)
+    clean_o, clean_l = d.result()
+    pt = b.page_table.copy()
+    pt[1, 0] = b.num_pages + 3
+    pt[3, 0] = -1
+    d.page_table.copy_(torch.from_numpy(pt).cuda())
+    cl = b.ctx_lens.copy()
+    cl[4] = C[4] - 1
+    cl[5] = b.pt_stride * 16 + 1
+    d.ctx_lens.copy_(torch.from_numpy(cl).cuda())
+    d.out.fill_(0)
+    d.lse.fill_(0)
+    d.prefill(max_q=300)
+    out, lse = d.result()
+    cq = b.cu_q
+    for r in range(b.B):
+        o, l = out[cq[r]:cq[r + 1]], lse[cq[r]:cq[r + 1]]
+        if r in (0, 2):
+            assert np.array_equal(o, clean_o[cq[r]:cq[r + 1]]) and np.array_equal(l, clean_l[cq[r]:cq[r + 1]]), r
+        else:
+            assert np.all(np.isnan(o)) and np.all(np.isnan(l)), r
+    ref_o, ref_l = oracle.attend_batch(b, [0, 2])
+    idx = np.concatenate([np.arange(cq[0], cq[1]), np.arange(cq[2], cq[3])])
+    eo, el = float(np.max(np.abs(out[idx] - ref_o))), float(np.max(np.abs(lse[idx] - ref_l)))
+    print(f"{spec.family} fail-closed good rows: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE

@@ -404,4 +404,9 @@ def test_kv_append_fails_closed():
     untouched = np.ones(kp.shape, bool)
     untouched[2, :, 10:16] = False
     assert np.all(kp2[untouched] == 0)
+    # a declared bound max_new below row 0's 30 new tokens: that row writes nothing either
+    kp3, _, skipped3 = oracle.kv_append(Hkv, hd, P, cu, L, pt, 4, k_new, None, kp, None, max_new=29)
+    assert skipped3 == 30 + 5 and np.all(kp3 == 0)
+    kp4, _, skipped4 = oracle.kv_append(Hkv, hd, P, cu, L, pt, 4, k_new, None, kp, None, max_new=30)
+    assert skipped4 == skipped and np.array_equal(kp4, kp2)
 
