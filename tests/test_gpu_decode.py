@@ -295,10 +295,10 @@ def _probe_batch(spec, t_star, key, n_filler=0, pt_stride=None, code_of=None):
 HD512_SHAPES = {  # name: (kv_shared, split, filler rows, max_ctx, pt_stride) -> items = slots * 4 * rows
     "global-4waves-32k": (False, 512, 0, None, None),        # 6 x 4 = 24 items
     "global-4waves-16k": (False, 512, 1, 20000, 1250),       # 40 x 4 x 2 = 320 items
-    "global-1wave": (False, 512, 8, 8192, None),              # 16 x 4 x 9 = 576 items
+    "global-1wave": (False, 512, 8, 8192, 512),               # 16 x 4 x 9 = 576 items
     "kv-shared-4waves-32k": (True, 1024, 0, None, None),     # 3 x 4 = 12 items
     "kv-shared-4waves-16k": (True, 1024, 1, 40000, 2500),    # 40 x 4 x 2 = 320 items
-    "kv-shared-1wave": (True, 1024, 8, 16384, None),         # 16 x 4 x 9 = 576 items
+    "kv-shared-1wave": (True, 1024, 8, 16384, 1024),         # 16 x 4 x 9 = 576 items
 }
 
 
