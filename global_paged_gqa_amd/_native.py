@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 LOCAL, GLOBAL = 0, 1
 OK, ERR_NULL_PTR, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_BAD_SPLIT, ERR_HIP = range(7)
 PAGE_SIZE = 16
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # GATTN_NOALLOC_SCRATCH_BYTES
 
 c_int, c_i64, c_size, c_vp, c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
@@ -84,6 +85,9 @@ _lib.gattn_decode_workspace_bytes.argtypes = [ctypes.POINTER(Layer), c_int, c_in
 _lib.gattn_decode.restype = c_int
 _lib.gattn_decode.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_int, c_int,
                               c_int, c_vp, c_size, c_vp, c_vp, c_vp]
+_lib.gattn_decode_noalloc.restype = c_int
+_lib.gattn_decode_noalloc.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_int, c_int,
+                                      c_int, c_vp, c_vp, c_vp]
 _lib.gattn_decode_fp8kv.restype = c_int
 _lib.gattn_decode_fp8kv.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_float, c_float, c_i64, c_vp, c_int,
                                     c_vp, c_int, c_int, c_int, c_vp, c_size, c_vp, c_vp, c_vp]
@@ -135,6 +139,14 @@ def gattn_decode(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, ctx
     _check(rc, "gattn_decode")
 
 
+def gattn_decode_noalloc(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, ctx_lens, batch, max_ctx,
+                         split_tokens, out, lse, stream=None):
+    rc = _lib.gattn_decode_noalloc(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), int(num_pages),
+                                   _addr(page_table), int(pt_stride), _addr(ctx_lens), int(batch), int(max_ctx),
+                                   int(split_tokens), _addr(out), _addr(lse), _stream(stream))
+    _check(rc, "gattn_decode_noalloc")
+
+
 def gattn_decode_fp8kv(layer, q, k_pool, v_pool, k_scale, v_scale, num_pages, page_table, pt_stride, ctx_lens,
                        batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream=None):
     rc = _lib.gattn_decode_fp8kv(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), float(k_scale),
@@ -178,6 +190,7 @@ def gattn_combine(batch, num_q_heads, head_dim, num_splits, o_part, lse_part, ou
 def exported_symbols():
     """Names the shared library exports (for the ABI check)."""
     return sorted(n for n in ("gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
-                              "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
+                              "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_noalloc",
+                              "gattn_decode_fp8kv", "gattn_prefill",
                               "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8")
                   if hasattr(_lib, n))

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
-SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip", "append.hip"]
+SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip", "append.hip", "noalloc.hip"]
 # Per-source extra hipcc flags (none at present: the kernels keep their MFMA accumulators
 # in AGPRs, which leaves the VGPRs to operand prefetch).
 EXTRA = {}

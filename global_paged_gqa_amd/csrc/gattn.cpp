@@ -128,7 +128,7 @@ namespace {
 int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool, const void *v_pool, bool fp8,
                 float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
                 const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
-                size_t workspace_bytes, uint16_t *out, float *lse, void *stream) {
+                size_t workspace_bytes, uint16_t *out, float *lse, void *stream, bool noalloc = false) {
     int rc = check_layer(layer);
     if (rc != GATTN_OK)
         return rc;
@@ -160,6 +160,15 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
     if (rc != GATTN_OK)
         return rc;
     const size_t need = workspace_for(layer, batch, plan);
+    if (noalloc) {
+        // the partials go to this device's fixed scratch array (looked up after every check)
+        if (need > GATTN_NOALLOC_SCRATCH_BYTES)
+            return GATTN_ERR_WORKSPACE_TOO_SMALL;
+        if (batch == 0)
+            return GATTN_OK;
+        if (need > 0 && gattn::noalloc_scratch(&workspace, &workspace_bytes) != hipSuccess)
+            return GATTN_ERR_HIP;
+    }
     if (need > workspace_bytes)
         return GATTN_ERR_WORKSPACE_TOO_SMALL;
     if (need > 0 && !workspace)
@@ -219,6 +228,13 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
                  uint16_t *out, float *lse, void *stream) {
     return decode_impl(layer, q, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride, ctx_lens,
                        batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream);
+}
+
+int gattn_decode_noalloc(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                         int64_t num_pages, const int32_t *page_table, int pt_stride, const int32_t *ctx_lens,
+                         int batch, int max_ctx, int split_tokens, uint16_t *out, float *lse, void *stream) {
+    return decode_impl(layer, q, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride, ctx_lens,
+                       batch, max_ctx, split_tokens, nullptr, 0, out, lse, stream, true);
 }
 
 int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,

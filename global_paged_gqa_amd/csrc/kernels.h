@@ -75,4 +75,8 @@ hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_spli
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, bool kv_shared, int batch,
                           hipStream_t stream);
 
+// Device address and size of the current device's copy of the no-allocation decode's scratch
+// (looked up on the first call per device, then cached).
+hipError_t noalloc_scratch(void **ptr, size_t *bytes);
+
 }  // namespace gattn

@@ -35,8 +35,9 @@
  *
  * Ownership. The caller allocates every buffer (device memory unless noted) and
  * keeps it alive until the work on `stream` has finished. The library never
- * allocates, frees or synchronises, keeps no mutable global state, and is safe
- * to call from several host threads. `stream` is a hipStream_t (NULL = the
+ * allocates, frees or synchronises, keeps no mutable global state (apart from
+ * gattn_decode_noalloc's per-GPU scratch, below), and is safe to call from
+ * several host threads. `stream` is a hipStream_t (NULL = the
  * default stream); every call only enqueues work on it.
  *
  * Errors. Argument errors are detected on the host before anything is enqueued
@@ -59,6 +60,8 @@ extern "C" {
 
 #define GATTN_ABI_VERSION 1
 #define GATTN_PAGE_SIZE 16
+/* Size of the per-GPU device array that holds gattn_decode_noalloc's split partials. */
+#define GATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 * 1024 * 1024)
 
 enum gattn_family { GATTN_LOCAL = 0, GATTN_GLOBAL = 1 };
 
@@ -158,6 +161,27 @@ int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_
                  const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
                  const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
                  size_t workspace_bytes, uint16_t *out, float *lse, void *stream);
+
+/*
+ * gattn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. It runs gattn_decode's kernels with the split partials
+ * in a fixed device array that the library holds on every GPU it runs on
+ * (GATTN_NOALLOC_SCRATCH_BYTES, 64 MiB, kept until the process ends), and it
+ * allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ * Arguments, outputs, errors and results are exactly gattn_decode's, bit for
+ * bit. A call whose partials would not fit the array
+ * (gattn_decode_workspace_bytes(...) > GATTN_NOALLOC_SCRATCH_BYTES) returns
+ * GATTN_ERR_WORKSPACE_TOO_SMALL with nothing enqueued. All calls on one GPU share
+ * that GPU's array and it keeps the last call's contents: calls that overlap on
+ * one GPU (other streams or host threads) race, and the caller must order them.
+ * The first call on a device looks up that device's array address with the
+ * device current and caches it; a failed lookup returns GATTN_ERR_HIP.
+ */
+int gattn_decode_noalloc(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
+                         const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                         const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, uint16_t *out,
+                         float *lse, void *stream);
 
 /*
  * gattn_decode over an FP8 KV pool (the pegainfer "[Model] Gemma 4 M2 26B-A4B" plan's opt-in

@@ -27,8 +27,9 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
-                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_fp8kv", "gattn_prefill",
-                            "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8"])
+                            "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_noalloc",
+                            "gattn_decode_fp8kv", "gattn_prefill", "gattn_combine", "gattn_kv_append",
+                            "gattn_kv_append_fp8"])
     for n in names:
         assert hasattr(nat._lib, n), n
     assert g.gattn_abi_version() == 1
@@ -142,6 +143,47 @@ def _decode_status(**over):
 def test_decode_rejects_bad_arguments_without_a_device(over, status):
     assert _decode_status(**over) == status
     assert _decode_status(batch=0) == 0  # no sticky state after a rejected call
+
+
+def _noalloc_status(**over):
+    lay = over.pop("layer", g.make_layer("global", 32, 4, 512))
+    args = dict(q=1 << 20, k_pool=2 << 20, v_pool=3 << 20, num_pages=100, page_table=4 << 20, pt_stride=512,
+                ctx_lens=5 << 20, batch=32, max_ctx=8192, split_tokens=512, out=7 << 20, lse=8 << 20)
+    args.update(over)
+    try:
+        g.gattn_decode_noalloc(lay, **args, stream=0)
+    except g.GattnError as e:
+        return e.status
+    return 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), nat.ERR_NULL_PTR),
+    (dict(v_pool=None), nat.ERR_NULL_PTR),
+    (dict(lse=None), nat.ERR_NULL_PTR),
+    (dict(batch=-1), nat.ERR_BAD_SHAPE),
+    (dict(pt_stride=511), nat.ERR_BAD_SHAPE),
+    (dict(split_tokens=500), nat.ERR_BAD_SPLIT),
+    (dict(layer=g.make_layer("global", 32, 4, 128)), nat.ERR_UNSUPPORTED),
+    # partials of 1000 rows x 32 heads x 16 splits x 513 words = 1.05 GB > the 64 MiB scratch
+    (dict(batch=1000), nat.ERR_WORKSPACE_TOO_SMALL),
+    (dict(batch=0), 0),
+    (dict(batch=0, split_tokens=0), 0),
+])
+def test_decode_noalloc_rejects_bad_arguments_without_a_device(over, status):
+    """The no-allocation decode checks its arguments exactly as gattn_decode does, and rejects a call
+    whose partials would not fit its fixed scratch, all before any HIP call."""
+    assert _noalloc_status(**over) == status
+
+
+def test_noalloc_scratch_limit():
+    lay = g.make_layer("global", 32, 4, 512)
+    assert nat.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the largest batch of the 8192-context global workload at split 512 that fits: 63 rows
+    per_row = g.gattn_decode_workspace_bytes(lay, 1, 8192, 512)
+    fit = nat.NOALLOC_SCRATCH_BYTES // per_row
+    assert fit == 63
+    assert _noalloc_status(batch=fit + 1) == nat.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_prefill_and_combine_reject_bad_arguments():
