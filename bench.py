@@ -1,15 +1,19 @@
 """Benchmark of the hybrid paged GQA attention hot path on one MI355X.
 
-Workload (the metric's configuration): global-family split-KV decode, batch 32,
-32 query heads, 4 KV heads, head_dim 512, ragged contexts ~ U{1..8192}, page
-size 16, globally shuffled page tables, 512-token splits, bf16 N(0,1) inputs.
-One step = one gattn_decode call (split kernel + logsumexp combine) with every
-input resident in HBM. The prefill half of the metric is measured on the mixed
-step's prefill rows (4 chunks of 2048 queries, priors ~ U{0..6144}, global and
-local families) and reported alongside.
+Headline workload (the largest configuration that fits one GPU): the 60-layer decode sweep of
+a Gemma-4-31B-shaped stack, five local layers then one global layer, ten times, ending on a
+global layer. 16 rows at 32768 tokens of context; local layers: head_dim 256, 16 KV heads,
+1024-token window (only window pages backed), 512-token splits; global layers: head_dim 512,
+4 KV heads, V read from the K cache (K=V), 1024-token splits; 32 query heads, pages of 16
+tokens, globally shuffled page tables, bf16 N(0,1) pools filled on the device. One step = the
+60 back-to-back gattn_decode calls (split kernels and logsumexp combines) with every input
+resident in HBM (about 34 GB of pools).
 
-Prints one JSON line (rank 0). value = decode KV GB/s over the timed steps:
-KV bytes = sum over rows and KV heads of visible keys * head_dim * 2 B * 2 (K, V).
+Prints one JSON line. value = decode KV GB/s over the timed steps: KV bytes = sum over layers,
+rows and KV heads of visible keys * head_dim * 2 B * (1 with K=V, else 2). The other
+configurations (tiny decode, the 32-row global decode, the 64-row local decode, the mixed
+prefill + decode step of both families, the 65536-token row, FP8 pools, the 12B geometry, KV
+append) are sub-records of the same line, with the fp64 oracle timed on the host's cores for each.
 """
 import argparse
 import json
@@ -23,17 +27,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% bf16 MFMA peak)"
-DECODE_KERNEL = "decode_split_kernel<512, false, 1, 1, 32768>"
+SWEEP_GLOBAL_KERNEL = "decode_split_kernel<512, true, 1, 1, 32768>"
+CFG2_KERNEL = "decode_split_kernel<512, false, 1, 1, 32768>"
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--no-sweep", action="store_true", help="skip the local decode, 60-layer sweep and long run")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the 60-layer sweep (profiling runs of its kernels)")
     p.add_argument("--no-flushed", action="store_true",
                    help="skip the MALL-flushed re-measurement (profiling runs: keeps every decode launch "
                         "in the kernel trace identical to the timed ones)")
@@ -58,10 +64,10 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest):
-    """HBM bytes per decode-kernel launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "decode_global_b32_counters.txt")
+def measured_traffic(digest, key):
+    """HBM bytes per launch of one kernel (``key``, e.g. ``sweep_global``) from the committed counter
+    summary, if it was taken on the current decode source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -73,9 +79,38 @@ def measured_traffic(digest):
     if vals.get("kernel_source_digest") != digest:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"{key}_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def host_cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def shader_clock_mhz():
+    """The current shader clock level each GPU's driver reports (sysfs pp_dpm_sclk, the level marked
+    '*'), in MHz, or None where the file is not readable."""
+    import glob
+    import re
+    clocks = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    if m:
+                        clocks.append(int(m.group(1)))
+        except OSError:
+            continue
+    return clocks or None
 
 
 def calib_copy():
@@ -89,22 +124,25 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "launches": 5}))
 
 
-def cpu_baseline(batch, kv_bytes):
+def oracle_rate(batches, work, unit, min_s, what):
+    """Time the fp64 oracle (``oracle.attend_batch``) on host batches, repeating the set until
+    ``min_s`` seconds have passed; ``work`` is the algorithmic bytes or flops of one pass."""
     import oracle
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.attend_batch(batch)
+        for b, rows in batches:
+            oracle.attend_batch(b, rows)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or reps >= 50:
+        if el >= min_s or reps >= 50:
             break
-    return {"value": round(kv_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"the full 32-row global decode batch, {reps} pass(es) in {el:.1f} s "
-                      f"(fp64 two-pass softmax over contiguous K/V, OpenMP over (query, head))"}
+    scale = 1e9 if unit == "GB/s" else 1e9
+    return {"value": round(work * reps / el / scale, 3), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
+            "seconds": round(el, 2), "passes": reps,
+            "sample": f"{what}; fp64 two-pass softmax over contiguous K/V, OpenMP over (query, head)"}
 
 
-def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
+def prefill_measure(torch, devio, workloads, traffic, flush, batches, iters=10):
     """The mixed step of each family: its 4 prefill chunks alone (TFLOP/s), its 60 decode rows
     alone (GB/s) and the whole step, gattn_prefill then gattn_decode on one stream. Every timed
     run follows a 1 GiB write that flushes the MALL, outside the events."""
@@ -124,6 +162,7 @@ def prefill_measure(torch, devio, workloads, traffic, flush, iters=10):
 
     for fam in ("global", "local"):
         pre, dec = workloads.cfg4_mixed(fam)
+        batches[f"cfg4_{fam}"] = (pre, dec)
         d = devio.DeviceBatch(pre)
         dd = devio.DeviceBatch(dec)
         # warm-up: the first launches of a kernel run at a lower clock and miss its code caches
@@ -312,10 +351,9 @@ def gemma12b_measure(torch, devio, workloads, traffic, stream, flush, steps=50):
     return out
 
 
-def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
-    """The 60-layer decode sweep (5 local : 1 global, last global; 16 rows at 32768 tokens; global
-    layers K=V with 1024-token splits, local layers 512) with every layer's pools resident, timed
-    end to end and per family; then the 65536-token global K=V decode."""
+def build_sweep(torch, devio, workloads, traffic):
+    """The 60 layers of the decode sweep resident on the device (pools filled there), sharing one
+    workspace; returns (layers [(family, DeviceLayout)], layouts, KV bytes total and per family)."""
     nat = devio.nat
     n = workloads.SWEEP_LAYERS
     layers, lays, kv_total, kv_fam = [], [], 0, {"local": 0, "global": 0}
@@ -332,15 +370,30 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
     ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
     for _, d in layers:
         d.workspace, d.ws_bytes = ws, ws_bytes
+    return layers, lays, kv_total, kv_fam
 
-    def sweep():
-        for fam, d in layers:
-            d.decode(workloads.SWEEP_SPLIT[fam])
 
-    sweep()
+def combine_time(torch, nat, d, split, stream, n=50):
+    """Mean duration of the logsumexp combine alone on the partials a DeviceLayout's last decode left in
+    its workspace (to separate the split kernel's own duration from the whole call)."""
+    lay, s = d.lay, d.lay.spec
+    ns = d.workspace_bytes(split) // (4 * (s.head_dim + 1) * lay.B * s.num_q_heads)
+    n_o = lay.B * s.num_q_heads * ns * s.head_dim
+    o_part, lse_part = d.workspace[:n_o], d.workspace[n_o:n_o + lay.B * s.num_q_heads * ns]
+    evs = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nat.gattn_combine(lay.B, s.num_q_heads, s.head_dim, ns, o_part, lse_part, d.out, d.lse, stream)
+        e1.record(stream)
+        evs.append((e0, e1))
     torch.cuda.synchronize()
-    t = median(event_times(torch, stream, sweep, reps))
-    # per layer: events around every call of one more sweep
+    return sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / n
+
+
+def sweep_extras(torch, devio, workloads, traffic, stream, layers, lays, kv_total, kv_fam, t_sweep, reps=10):
+    """Per-family layer times, the sweep captured in a HIP graph, and the sweep over FP8 pools."""
+    out = {}
     evs = []
     for fam, d in layers:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -352,10 +405,13 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
     per = {"local": 0.0, "global": 0.0}
     for fam, e0, e1 in evs:
         per[fam] += e0.elapsed_time(e1) * 1e-3
-    out = {"workload": "60-layer decode sweep (LLLLLG x10), 16 rows x 32768 tokens; global: hd 512, 4 KV "
-                       "heads, K=V, split 1024; local: hd 256, 16 KV heads, window 1024, split 512",
-           "kv_bytes": kv_total, "ms": round(t * 1e3, 4), "gbs": round(kv_total / t / 1e9, 1),
-           "frac": round(kv_total / t / 1e9 / HBM_PEAK_GBS, 4)}
+    for fam in ("local", "global"):
+        out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
+        out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
+
+    def sweep():
+        for fam, d in layers:
+            d.decode(workloads.SWEEP_SPLIT[fam])
     # the same 60 calls captured once in a HIP graph and replayed (no launch gaps between layers)
     try:
         graph = torch.cuda.CUDAGraph()
@@ -375,12 +431,9 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
         del graph
     except Exception as e:  # report, never hide
         out["graph_error"] = str(e)[:200]
-    for fam in ("local", "global"):
-        out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
-        out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
-    # the same sweep with the 50 local layers' K/V in FP8 (E4M3) pools (gattn_decode_fp8kv): half their bytes
-    layers8 = None
+    # the same sweep with the 50 local layers' K/V in FP8 (E4M3) pools (gattn_decode_fp8kv), then every layer
     try:
+        ws = layers[0][1].workspace
         layers8 = []
         for (fam, d), lay in zip(layers, lays):
             if fam == "local":
@@ -396,26 +449,28 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
         t8 = median(event_times(torch, stream, sweep8, reps))
         kv8 = kv_fam["global"] + kv_fam["local"] // 2
         out["fp8_local"] = {"kv_bytes": kv8, "ms": round(t8 * 1e3, 4), "gbs": round(kv8 / t8 / 1e9, 1),
-                            "speedup_vs_bf16": round(t / t8, 3)}
-        # every layer in FP8: the global layers' K=V pools too (their one scale serves K and V)
-        del layers
-        layers = []
+                            "speedup_vs_bf16": round(t_sweep / t8, 3)}
+        layers.clear()  # the bf16 local pools are not used again: drop them before the FP8 global pools
+        all8 = []
         for (fam, d), lay in zip(layers8, lays):
             if fam == "global":
                 d = devio.DeviceLayout(lay, workloads.fill_e4m3_device, workspace=ws,
                                        fp8=(workloads.FP8_K_SCALE, workloads.FP8_K_SCALE))
-            layers.append((fam, d))
-        layers8 = layers
+            all8.append((fam, d))
+        layers8 = all8
         sweep8()
         torch.cuda.synchronize()
         ta = median(event_times(torch, stream, sweep8, reps))
         out["fp8_all"] = {"kv_bytes": kv_total // 2, "ms": round(ta * 1e3, 4),
-                          "gbs": round(kv_total // 2 / ta / 1e9, 1), "speedup_vs_bf16": round(t / ta, 3)}
+                          "gbs": round(kv_total // 2 / ta / 1e9, 1), "speedup_vs_bf16": round(t_sweep / ta, 3)}
+        del layers8, all8
     except Exception as e:  # report, never hide
         out["fp8_error"] = str(e)[:200]
-    layers = layers8 = ws = None
-    torch.cuda.empty_cache()
+    return out
 
+
+def long_measure(torch, devio, workloads, traffic, stream, flush):
+    """The single 65536-token global decode row (K=V, split 1024)."""
     lay = workloads.long_global_decode(rows=())
     d = devio.DeviceLayout(lay, workloads.fill_normal_bf16_device)
     s = lay.spec
@@ -424,10 +479,88 @@ def sweep_measure(torch, devio, workloads, traffic, stream, flush, reps=10):
         d.decode(1024)
     tl = median(event_times(torch, stream, lambda: d.decode(1024), 50))
     tlf = median(event_times(torch, stream, lambda: d.decode(1024), 10, flush))
-    long = {"workload": "one 65536-token global decode row, K=V, split 1024", "kv_bytes": kv,
-            "us": round(tl * 1e6, 2), "gbs": round(kv / tl / 1e9, 1),
+    tc = combine_time(torch, devio.nat, d, 1024, stream)
+    return {"workload": "one 65536-token global decode row, K=V, split 1024", "kv_bytes": kv,
+            "us": round(tl * 1e6, 2), "gbs": round(kv / tl / 1e9, 1), "frac": round(kv / tl / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_gbs": round(kv / (tl - tc) / 1e9, 1), "combine_us": round(tc * 1e6, 2),
             "mall_flushed_us": round(tlf * 1e6, 2), "mall_flushed_gbs": round(kv / tlf / 1e9, 1)}
-    return out, long
+
+
+def cfg2_measure(torch, devio, workloads, traffic, stream, flush, digest, steps=200):
+    """The 32-row global decode batch (32 q heads, 4 KV heads, hd 512, contexts ~U{1..8192}, split 512):
+    whole call, split kernel alone (call minus the combine's own time) and after a MALL flush."""
+    batch = workloads.cfg2_global_decode()
+    s = batch.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, batch.ctx_lens)
+    d = devio.DeviceBatch(batch)
+    for _ in range(20):
+        d.decode(512)
+    torch.cuda.synchronize()
+    t = median(event_times(torch, stream, lambda: d.decode(512), steps))
+    tf = median(event_times(torch, stream, lambda: d.decode(512), 20, flush))
+    nat = devio.nat
+    ns = nat.gattn_decode_workspace_bytes(d.layer, batch.B, int(batch.ctx_lens.max()), 512) // (
+        4 * (s.head_dim + 1) * batch.B * s.num_q_heads)
+    n_o = batch.B * s.num_q_heads * ns * s.head_dim
+    evs = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        nat.gattn_combine(batch.B, s.num_q_heads, s.head_dim, ns, d.workspace[:n_o], d.workspace[n_o:], d.out, d.lse,
+                          stream)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    tc = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / len(evs)
+    return batch, {"workload": "global decode: batch 32, 32 q heads, 4 KV heads, head_dim 512, contexts "
+                               "~U{1..8192}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
+                   "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
+                   "kernel": CFG2_KERNEL, "kernel_us": round((t - tc) * 1e6, 2),
+                   "kernel_gbs": round(kv / (t - tc) / 1e9, 1), "combine_us": round(tc * 1e6, 2),
+                   "traffic": measured_traffic(digest, "cfg2"),
+                   "mall_flushed_gbs": round(kv / tf / 1e9, 1), "mall_flushed_frac": round(kv / tf / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baselines(workloads, traffic, batches):
+    """The fp64 oracle on each configuration's rows (or a stated sample of them), timed on the host's
+    cores, as the same algorithmic GB/s or GFLOP/s the GPU figures use."""
+    out = {}
+    b1 = workloads.cfg1_tiny_decode()
+    s = b1.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, b1.ctx_lens)
+    out["tiny_decode"] = oracle_rate([(b1, None)], kv, "GB/s", 2.0, "the whole tiny decode (1 row, L 1025)")
+    b2 = batches.get("cfg2") or workloads.cfg2_global_decode()
+    s = b2.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, b2.ctx_lens)
+    out["global_decode"] = oracle_rate([(b2, None)], kv, "GB/s", 4.0, "the whole 32-row global decode batch")
+    b3 = workloads.cfg3_local_decode()
+    s = b3.spec
+    kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, b3.ctx_lens)
+    out["local_decode"] = oracle_rate([(b3, None)], kv, "GB/s", 4.0, "the whole 64-row local decode batch")
+    for fam in ("global", "local"):
+        pre, dec = batches.get(f"cfg4_{fam}") or workloads.cfg4_mixed(fam)
+        s = pre.spec
+        r = int(pre.ctx_lens.argmin())  # the row with the shortest prior (least oracle time)
+        fl = traffic.prefill_flops(s.is_global, s.window, s.num_q_heads, s.head_dim, pre.ctx_lens[[r]],
+                                   pre.q_lens[[r]])
+        rec = oracle_rate([(pre, [r])], fl, "GFLOP/s", 1.0,
+                          f"{fam} mixed step: prefill row {r} (2048 queries after a prior of "
+                          f"{int(pre.ctx_lens[r] - pre.q_lens[r])})")
+        kv = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared, dec.ctx_lens)
+        rec["decode_rows"] = oracle_rate([(dec, None)], kv, "GB/s", 2.0, f"{fam} mixed step: its 60 decode rows")
+        out[f"mixed_{fam}"] = rec
+    # the sweep: sampled rows of one global and one local layer, weighted as in the sweep (10 : 50)
+    g = workloads.sweep_layer(5, "global", rows=(0, 1))
+    l0 = workloads.sweep_layer(0, "local", rows=tuple(range(workloads.SWEEP_B)))
+    kv_g = traffic.decode_kv_bytes(True, 0, 4, 512, True, g.host.ctx_lens)
+    kv_l = traffic.decode_kv_bytes(False, 1024, 16, 256, False, l0.host.ctx_lens)
+    out["sweep"] = oracle_rate([(g.host, None)] + [(l0.host, None)] * 5, kv_g + 5 * kv_l, "GB/s", 8.0,
+                               "sampled sweep rows: rows 0-1 of global layer 5 (K=V, 32768 tokens) once and all 16 "
+                               "rows of local layer 0 five times (the sweep's 10 : 50 layer mix)")
+    lg = workloads.long_global_decode(rows=(0,))
+    kv = traffic.decode_kv_bytes(True, 0, 4, 512, True, lg.host.ctx_lens)
+    out["long_decode"] = oracle_rate([(lg.host, None)], kv, "GB/s", 2.0, "the whole 65536-token row")
+    return out
 
 
 def main():
@@ -436,6 +569,7 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
               "path: rows shard across GPUs with no attention-side communication.", file=sys.stderr)
         sys.exit(2)
+    cpu_model = host_cpu_model()
     import torch
     if args.calib_copy:
         calib_copy()
@@ -446,65 +580,42 @@ def main():
     import workloads
     from global_paged_gqa_amd import devio, traffic
 
-    batch = workloads.cfg2_global_decode()
-    s = batch.spec
-    split = 512
-    kv_bytes = traffic.decode_kv_bytes(s.is_global, s.window, s.num_kv_heads, s.head_dim, s.kv_shared,
-                                       batch.ctx_lens)
-    d = devio.DeviceBatch(batch)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        d.decode(split)
-    torch.cuda.synchronize()
+    digest = kernel_source_digest()
+    layers, lays, kv_total, kv_fam = build_sweep(torch, devio, workloads, traffic)
 
-    # timed region: exactly `steps` back-to-back steps, per-step events on the library's stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    def sweep(global_events=None):
+        for fam, d in layers:
+            if global_events is not None and fam == "global":
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                d.decode(workloads.SWEEP_SPLIT[fam])
+                e1.record(stream)
+                global_events.append((e0, e1))
+            else:
+                d.decode(workloads.SWEEP_SPLIT[fam])
+
+    for _ in range(args.warmup):
+        sweep()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` sweeps back to back; events around every global-layer call (the
+    # dominant kernel) on the library's stream
+    gev = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        d.decode(split)
-        e1.record(stream)
+    for _ in range(args.steps):
+        sweep(gev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_s = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
-    ms_per_step = wall / args.steps * 1e3
-    value = kv_bytes * args.steps / wall / 1e9
-
-    # the combine alone on the same partials, to separate the split kernel's own duration
-    nat = devio.nat
-    ns = nat.gattn_decode_workspace_bytes(d.layer, batch.B, int(batch.ctx_lens.max()), split) // (4 * (s.head_dim + 1) * batch.B * s.num_q_heads)
-    o_part = d.workspace[: batch.B * s.num_q_heads * ns * s.head_dim]
-    lse_part = d.workspace[batch.B * s.num_q_heads * ns * s.head_dim:]
-    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-    for e0, e1 in cevs:
-        e0.record(stream)
-        nat.gattn_combine(batch.B, s.num_q_heads, s.head_dim, ns, o_part, lse_part, d.out, d.lse, stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    combine_s = sum(e0.elapsed_time(e1) for e0, e1 in cevs) * 1e-3 / len(cevs)
-    split_kernel_s = sum(step_s) / len(step_s) - combine_s
-    achieved = kv_bytes / split_kernel_s / 1e9
-
-    # the same step with the 256 MB MALL flushed before each launch (outside the events)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    flushed = None
-    if not args.no_flushed:
-        fl = []
-        for _ in range(20):
-            flush.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            d.decode(split)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            fl.append(e0.elapsed_time(e1) * 1e-3)
-        fl.sort()
-        fgbs = kv_bytes / fl[len(fl) // 2] / 1e9
-        flushed = {"decode_gbs": round(fgbs, 1), "frac": round(fgbs / HBM_PEAK_GBS, 4)}
-
-    digest = kernel_source_digest()
-    traffic_bytes = measured_traffic(digest)
+    clock = shader_clock_mhz()
+    t_sweep = wall / args.steps
+    value = kv_total / t_sweep / 1e9
+    g_call = sum(a.elapsed_time(b) for a, b in gev) * 1e-3 / len(gev)
+    gd = [d for fam, d in layers if fam == "global"][-1]
+    g_comb = combine_time(torch, devio.nat, gd, workloads.SWEEP_SPLIT["global"], stream)
+    g_kernel = g_call - g_comb
+    kv_glayer = kv_fam["global"] // 10
+    achieved = kv_glayer / g_kernel / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -512,48 +623,68 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(t_sweep * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "global-family split-KV decode: batch 32, 32 q heads, 4 KV heads, head_dim 512, "
-                               "contexts ~U{1..8192}, page 16, shuffled pages, split 512",
-                   "batch": batch.B, "head_dim": s.head_dim, "num_q_heads": s.num_q_heads,
-                   "num_kv_heads": s.num_kv_heads, "split_tokens": split,
-                   "kv_bytes_per_step": kv_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(achieved, 1),
+        "config": {"workload": "60-layer decode sweep (LLLLLG x10, last layer global), 16 rows x 32768 tokens, "
+                               "32 q heads; local: hd 256, 16 KV heads, window 1024, split 512; global: hd 512, "
+                               "4 KV heads, K=V, split 1024; page 16, shuffled pages, bf16 N(0,1) pools",
+                   "layers": workloads.SWEEP_LAYERS, "batch": workloads.SWEEP_B, "context": workloads.SWEEP_L,
+                   "kv_bytes_per_step": kv_total, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": SWEEP_GLOBAL_KERNEL, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_bytes, "kernel_us": round(split_kernel_s * 1e6, 2),
-                     "combine_us": round(combine_s * 1e6, 2), "kernel_source_digest": digest},
-        "mall_flushed": flushed,
+                     "traffic": measured_traffic(digest, "sweep_global"),
+                     "bytes_per_launch": kv_glayer, "kernel_us": round(g_kernel * 1e6, 2),
+                     "call_us": round(g_call * 1e6, 2), "combine_us": round(g_comb * 1e6, 2),
+                     "kernel_source_digest": digest},
+        "host": {"cpu_model": cpu_model, "shader_clock_mhz_after_timed_region": clock},
     }
+    sw = {}
+    if not args.headline_only:
+        try:
+            sw = sweep_extras(torch, devio, workloads, traffic, stream, layers, lays, kv_total, kv_fam, t_sweep)
+        except Exception as e:  # report, never hide
+            sw = {"error": str(e)[:300]}
+    result["sweep"] = dict(sw, kv_bytes=kv_total, ms=round(t_sweep * 1e3, 4), gbs=round(value, 1))
+    layers = lays = gd = None
+    torch.cuda.empty_cache()
+    if args.headline_only:
+        print(json.dumps(result), flush=True)
+        return
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    batches = {}
+    for name, fn in (("long_decode", lambda: long_measure(torch, devio, workloads, traffic, stream, flush)),
+                     ("local_decode", lambda: local_decode_measure(torch, devio, workloads, traffic, stream, flush)),
+                     ("global_decode_fp8", lambda: global_fp8_measure(torch, devio, workloads, traffic, stream,
+                                                                      flush)),
+                     ("gemma12b", lambda: gemma12b_measure(torch, devio, workloads, traffic, stream, flush))):
+        try:
+            result[name] = fn()
+        except Exception as e:  # report, never hide
+            result[name] = {"error": str(e)[:300]}
+        torch.cuda.empty_cache()
+    try:
+        batches["cfg2"], result["global_decode"] = cfg2_measure(torch, devio, workloads, traffic, stream, flush,
+                                                                digest)
+    except Exception as e:  # report, never hide
+        result["global_decode"] = {"error": str(e)[:300]}
     if not args.no_prefill:
         try:
-            result["prefill"] = prefill_measure(torch, devio, workloads, traffic, flush)
+            result["prefill"] = prefill_measure(torch, devio, workloads, traffic, flush, batches)
         except Exception as e:  # report, never hide
             result["prefill"] = {"error": str(e)[:200]}
     try:
         result["kv_append"] = append_measure(torch, devio, workloads, stream, flush)
     except Exception as e:  # report, never hide
         result["kv_append"] = {"error": str(e)[:200]}
-    if not args.no_sweep:
-        try:
-            result["local_decode"] = local_decode_measure(torch, devio, workloads, traffic, stream, flush)
-            result["sweep"], result["long_decode"] = sweep_measure(torch, devio, workloads, traffic, stream, flush)
-        except Exception as e:  # report, never hide
-            result["sweep"] = {"error": str(e)[:300]}
-        try:
-            result["global_decode_fp8"] = global_fp8_measure(torch, devio, workloads, traffic, stream, flush)
-        except Exception as e:  # report, never hide
-            result["global_decode_fp8"] = {"error": str(e)[:300]}
-        try:
-            result["gemma12b"] = gemma12b_measure(torch, devio, workloads, traffic, stream, flush)
-        except Exception as e:  # report, never hide
-            result["gemma12b"] = {"error": str(e)[:300]}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(batch, kv_bytes)
+        base = cpu_baselines(workloads, traffic, batches)
+        result["cpu_baseline"] = dict(base["sweep"], host_cpu=cpu_model)
+        result["cpu_baselines"] = base
     print(json.dumps(result), flush=True)
 
 
