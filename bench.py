@@ -145,13 +145,13 @@ def oracle_rate(batches, work, unit, min_s, what):
 def prefill_measure(torch, devio, workloads, traffic, flush, batches, iters=10):
     """The mixed step of each family: its 4 prefill chunks alone (TFLOP/s), its 60 decode rows
     alone (GB/s) and the whole step, gattn_prefill then gattn_decode on one stream. Every timed
-    run follows a 1 GiB write that flushes the MALL, outside the events."""
+    run follows a MALL flush, outside the events."""
     out = {}
 
     def timed(fn):
         ts = []
         for _ in range(iters):
-            flush.zero_()
+            flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
@@ -195,62 +195,83 @@ def prefill_measure(torch, devio, workloads, traffic, flush, batches, iters=10):
 
 
 def append_measure(torch, devio, workloads, stream, flush, iters=20):
-    """gattn_kv_append of the mixed step's new tokens (the 4 x 2048 prefill chunks and the 60 decode
-    tokens) for each 31B family: GB/s of algorithmic bytes, every new K (and V) element read once
-    and written once; each timed run after a MALL flush."""
+    """gattn_kv_append of one mixed step's new tokens (the 4 x 2048 prefill chunks and the 60 decode
+    tokens, all 64 rows in one call) for each 31B family: GB/s of algorithmic bytes, every new K and
+    V element read once and written once; each timed run after a MALL flush. Beside it, a plain
+    device copy of the same bytes under the same flush (torch's copy of K and V into contiguous
+    buffers): the practical ceiling of a transfer of this size."""
     import numpy as np
     out = {}
     for fam in ("global", "local"):
         pre, dec = workloads.cfg4_mixed(fam)
-        s = pre.spec
-        rows = []
-        for b in (pre, dec):
-            d = devio.DeviceBatch(b)
-            n_new = b.q_lens.astype(np.int32)
-            cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
-            T = int(cu[-1])
-            kn = torch.randn(T, s.num_kv_heads, s.head_dim, device="cuda").to(torch.bfloat16).view(torch.int16)
-            vn = torch.randn_like(kn, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
-            rows.append((d, devio.dev(cu), kn, vn, b.B, int(n_new.max())))
-        nbytes = sum(kn.numel() * 2 * 2 * 2 for _, _, kn, _, _, _ in rows)  # K and V, read and written
+        b = workloads.concat_batches(pre, dec)
+        s = b.spec
+        d = devio.DeviceBatch(b)
+        n_new = b.q_lens.astype(np.int32)
+        cu = devio.dev(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32))
+        T, mx = int(n_new.sum()), int(n_new.max())
+        kn = torch.randn(T, s.num_kv_heads, s.head_dim, device="cuda").to(torch.bfloat16).view(torch.int16)
+        vn = torch.randn_like(kn, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        nbytes = kn.numel() * 2 * 2 * 2  # K and V, read and written
 
         def call():
-            for d, cu, kn, vn, B, mx in rows:
-                devio.nat.gattn_kv_append(d.layer, kn, vn, d.k_pool, d.v_pool, d.num_pages, d.page_table,
-                                          d.pt_stride, cu, d.ctx_lens, B, mx, None)
+            devio.nat.gattn_kv_append(d.layer, kn, vn, d.k_pool, d.v_pool, d.num_pages, d.page_table, d.pt_stride,
+                                      cu, d.ctx_lens, b.B, mx, None)
+        ck, cv = torch.empty_like(kn), torch.empty_like(vn)
+
+        def copy():
+            ck.copy_(kn)
+            cv.copy_(vn)
         for _ in range(5):
             call()
+            copy()
         t = median(event_times(torch, stream, call, iters, flush))
-        out[fam] = {"tokens": int(sum(kn.shape[0] for _, _, kn, _, _, _ in rows)), "bytes": nbytes,
-                    "us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1)}
+        tc = median(event_times(torch, stream, copy, iters, flush))
+        out[fam] = {"tokens": T, "rows": b.B, "bytes": nbytes, "us": round(t * 1e6, 2),
+                    "gbs": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "plain_copy_us": round(tc * 1e6, 2), "plain_copy_gbs": round(nbytes / tc / 1e9, 1)}
+        del ck, cv
         if fam == "local":  # the same tokens into E4M3 pools: 2 bytes read and 1 written per element
-            pools8 = [(torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda"),
-                       torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")) for d, *_ in rows]
-            nbytes8 = sum(kn.numel() * (2 + 1) * 2 for _, _, kn, _, _, _ in rows)
+            k8 = torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")
+            v8 = torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")
+            nbytes8 = kn.numel() * (2 + 1) * 2
 
             def call8():
-                for (d, cu, kn, vn, B, mx), (k8, v8) in zip(rows, pools8):
-                    devio.nat.gattn_kv_append_fp8(d.layer, kn, vn, k8, v8, workloads.FP8_K_SCALE,
-                                                  workloads.FP8_V_SCALE, d.num_pages, d.page_table, d.pt_stride, cu,
-                                                  d.ctx_lens, B, mx, None)
+                devio.nat.gattn_kv_append_fp8(d.layer, kn, vn, k8, v8, workloads.FP8_K_SCALE, workloads.FP8_V_SCALE,
+                                              d.num_pages, d.page_table, d.pt_stride, cu, d.ctx_lens, b.B, mx, None)
             for _ in range(5):
                 call8()
             t8 = median(event_times(torch, stream, call8, iters, flush))
             out["local_fp8"] = {"bytes": nbytes8, "us": round(t8 * 1e6, 2), "gbs": round(nbytes8 / t8 / 1e9, 1)}
-            del pools8
-        del rows
-    out["workload"] = ("gattn_kv_append of the mixed step's 8252 new tokens per family (4 prefill chunks of 2048, "
-                       "60 decode tokens) into the 31B pools, two calls")
+            del k8, v8
+        del d, kn, vn
+        torch.cuda.empty_cache()
+    out["workload"] = ("gattn_kv_append of the mixed step's 8252 new tokens per family (4 prefill chunks of 2048 and "
+                       "60 decode tokens, one call over the 64 rows) into the 31B pools")
     return out
 
 
+class MallFlush:
+    """Evicts the 256 MB MALL and the L2s by reading a 1 GiB buffer (a sum into one float), outside
+    the timed events. Reading leaves clean lines behind: a 1 GiB write would leave up to 256 MB of
+    dirty lines whose write-back the next, timed, kernel would pay for."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.torch.sum(self.buf, 0, out=self.out)
+
+
 def event_times(torch, stream, fn, n, flush=None):
-    """Per-call durations (s) of ``fn`` from HIP events recorded on ``stream``; with ``flush``, a
-    1 GiB buffer is overwritten before each call, outside the events."""
+    """Per-call durations (s) of ``fn`` from HIP events recorded on ``stream``; with ``flush`` (a
+    MallFlush), the caches are flushed before each call, outside the events."""
     ts = []
     for _ in range(n):
         if flush is not None:
-            flush.zero_()
+            flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -655,7 +676,7 @@ def main():
         print(json.dumps(result), flush=True)
         return
 
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush = MallFlush(torch)
     batches = {}
     for name, fn in (("long_decode", lambda: long_measure(torch, devio, workloads, traffic, stream, flush)),
                      ("local_decode", lambda: local_decode_measure(torch, devio, workloads, traffic, stream, flush)),

@@ -22,7 +22,7 @@ namespace gattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTok = 4;     // tokens per workgroup
+constexpr int kTok = 8;     // tokens per workgroup
 constexpr int kUnroll = 4;  // rows a lane loads before it stores them (loads in flight)
 
 // E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits) of the fp32 quotient x / scale

@@ -241,8 +241,11 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
  * or other devices' shares of one long context) merge the same way.
  * For each (row, head): M = max over splits of lse_s; LSE = M + ln sum_s
  * exp(lse_s - M); O = sum_s exp(lse_s - LSE) o_s. Splits with lse_s = -inf are
- * empty and are skipped (their o_s is never read). A row whose splits are all
- * empty gets O = 0 and LSE = -inf.
+ * empty and are skipped: their o_s may hold anything (stale data, NaN) and never
+ * enters the result, though the whole o_part buffer may be read. A row whose
+ * splits are all empty gets O = 0 and LSE = -inf; a NaN lse_s makes the (row,
+ * head) result NaN. The sums run in a fixed order over split indices, so the
+ * result depends only on the (row, head)'s own partials.
  *
  *   o_part     [batch][num_q_heads][num_splits][head_dim] fp32, each split's
  *              output already normalised by its own softmax sum.

@@ -238,14 +238,18 @@ def test_bad_lengths_and_pages_give_nan_rows_only(devio):
 
 
 # ------------------------------------------------------------------------ exported combine
-def test_combine_matches_fp64_merge(devio):
+@pytest.mark.parametrize("hd,ns", [(512, 7), (256, 3), (1024, 40), (512, 150), (4, 70)])
+def test_combine_matches_fp64_merge(devio, hd, ns):
+    """The exported merge at every launch shape: four split groups (head_dim <= 512) or two
+    (1024), 4, 8 or 16 splits in flight per thread, one pass or several (150 splits), split
+    LSEs read lane-parallel beyond the first 64."""
     import torch
     import global_paged_gqa_amd as g
-    rng = np.random.default_rng(5)
-    B, H, hd, ns = 3, 5, 512, 7
+    rng = np.random.default_rng(5 + ns)
+    B, H = 3, 5
     lse = rng.normal(0, 3, size=(B, H, ns)).astype(np.float32)
     lse[0, 0, :] = -np.inf
-    lse[1, 2, [0, 3, 6]] = -np.inf
+    lse[1, 2, [0, ns // 2, ns - 1]] = -np.inf
     o = (0.25 * rng.normal(size=(B, H, ns, hd))).astype(np.float32)   # attention-sized outputs
     o[lse == -np.inf] = np.nan          # empty splits must never be read
     out = torch.empty((B, H, hd), dtype=torch.int16, device="cuda")
@@ -260,6 +264,43 @@ def test_combine_matches_fp64_merge(devio):
     assert np.array_equal(fin, np.isfinite(got_l))
     assert np.max(np.abs(got_l[fin] - ref_l[fin])) < 1e-5
     assert np.max(np.abs(got_o - ref_o)) < 1e-2
+
+
+@pytest.mark.parametrize("n,hd", [(3, 512), (7, 512), (7, 1024), (7, 256)])
+def test_combine_bits_independent_of_slot_count(devio, n, hd):
+    """A (row, head)'s merged result is the same bit for bit whether its n splits sit in n slots
+    or are padded with empty (-inf) slots up to 150, across every launch shape the slot count
+    selects (thread groups 1, 2 or 4; 4, 8 or 16 loads in flight; one pass or several): the
+    sums run in a fixed order and skip empty splits, so one row's output never depends on the
+    batch's longest row. A NaN split LSE turns only its own (row, head) into NaN."""
+    import torch
+    import global_paged_gqa_amd as g
+    rng = np.random.default_rng(11 + n)
+    B, H = 2, 3
+    lse = rng.normal(0, 3, size=(B, H, n)).astype(np.float32)
+    o = (0.25 * rng.normal(size=(B, H, n, hd))).astype(np.float32)
+    lse[1, 1, n - 1] = np.nan
+
+    def run(ns):
+        lp = np.full((B, H, ns), -np.inf, np.float32)
+        op = np.full((B, H, ns, hd), np.nan, np.float32)
+        lp[..., :n], op[..., :n, :] = lse, o
+        out = torch.empty((B, H, hd), dtype=torch.int16, device="cuda")
+        lo = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        g.gattn_combine(B, H, hd, ns, torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(), out, lo)
+        return out.cpu().numpy(), lo.cpu().numpy()
+
+    base_o, base_l = run(n)
+    assert np.all(np.isnan(devio.host_bf16(torch.from_numpy(base_o))[1, 1])) and np.isnan(base_l[1, 1])
+    ok = np.ones((B, H), bool)
+    ok[1, 1] = False
+    assert np.all(np.isfinite(base_l[ok]))
+    for ns in (5, 8, 12, 20, 30, 40, 70, 150):
+        if ns < n:
+            continue
+        got_o, got_l = run(ns)
+        assert np.array_equal(got_o[ok], base_o[ok]) and np.array_equal(got_l[ok], base_l[ok]), ns
+        assert np.isnan(got_l[1, 1])
 
 
 # ------------------------------------------------------------------------ head_dim 512 index probes
