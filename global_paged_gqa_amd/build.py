@@ -13,9 +13,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
 SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip", "append.hip", "noalloc.hip"]
-# Per-source extra hipcc flags (none at present: the kernels keep their MFMA accumulators
-# in AGPRs, which leaves the VGPRs to operand prefetch).
-EXTRA = {}
+# Per-source extra hipcc flags. Decode: MFMA accumulators in VGPRs. Its softmax rescales the
+# O accumulators with vector multiplies; held in AGPRs, they were copied to VGPRs and back on
+# every page (a quarter of a page's instructions at head_dim 512). The prefill kernels keep
+# theirs in AGPRs, which leaves the VGPRs to operand prefetch.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 

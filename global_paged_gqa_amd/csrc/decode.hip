@@ -282,40 +282,51 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
 
         // ---- online softmax; lane holds S^T[token t0 + 4 r4 + e][head c16]. Tokens outside
         // [tb, te) are selected out (a NaN in an unused slot never reaches the sums).
-        bool valid[4];
         float mx = -INFINITY;
+        if (t0 >= tb && t0 + kPage <= te) {  // interior page: every token visible
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * r4 + e;
-            valid[e] = t >= tb && t < te;
-            st[e] = valid[e] ? st[e] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, st[e]);
+            for (int e = 0; e < 4; ++e) {
+                st[e] *= a.scale_log2;
+                mx = fmaxf(mx, st[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = t0 + 4 * r4 + e;
+                st[e] = (t >= tb && t < te) ? st[e] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, st[e]);
+            }
         }
         // Lazy rescale: a column keeps its reference maximum until a score exceeds it by more
         // than 2^8, so P stays below 256 and the accumulators are rescaled only on those pages.
         // O is normalised by the sum of the bf16-rounded weights the PV product uses, so a
         // weight's rounding scales numerator and denominator alike (a single dominant key gives
         // exactly its V row, whatever the reference); the LSE uses the sum of the fp32 weights.
-        // Both share the reference maximum.
-        const float m_new = fmaxf(m_run, rows_max4(mx));
-        const bool resc = m_new > m_run + kRescaleLog2;
-        const float alpha = resc ? fast_exp2(m_run - m_new) : 1.0f;
-        if (resc)
-            m_run = m_new;
+        // Both share the reference maximum. The weights are formed against the current
+        // reference while the column maxima are still being reduced, and formed again on the
+        // rare pages where a column moves its reference; the sums are taken after the PV
+        // product is issued. Only the order of independent work differs from forming them in
+        // sequence: the results are the same.
         float ps[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             ps[e] = fast_exp2(st[e] - m_run);
-        const u32x2 pb = {pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
-        const float rs = ((bf16_lo(pb[0]) + bf16_hi(pb[0])) + bf16_lo(pb[1])) + bf16_hi(pb[1]);
-        const float rx = ((ps[0] + ps[1]) + ps[2]) + ps[3];
-        l_run = l_run * alpha + rows_sum4(rs);
-        l_ex = l_ex * alpha + rows_sum4(rx);
+        const float m_new = fmaxf(m_run, rows_max4(mx));
+        const bool resc = m_new > m_run + kRescaleLog2;
+        float alpha = 1.0f;
         if (__builtin_amdgcn_ballot_w64(resc)) {
+            if (resc) {
+                alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ps[e] = fast_exp2(st[e] - m_run);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 acc[dt] *= alpha;
         }
+        const u32x2 pb = {pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
 
         // ---- O^T += V^T P^T over the whole head dimension
         const int uv = SHARED ? u : u + 1;
@@ -347,6 +358,10 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
             for (int dt = 0; dt < NDT; ++dt)
                 acc[dt] = mfma_k16(tr_read(vs + vbase[dt & 7] + 256 * (dt >> 3)), pb, acc[dt]);
         }
+        const float rs = ((bf16_lo(pb[0]) + bf16_hi(pb[0])) + bf16_lo(pb[1])) + bf16_hi(pb[1]);
+        const float rx = ((ps[0] + ps[1]) + ps[2]) + ps[3];
+        l_run = l_run * alpha + rows_sum4(rs);
+        l_ex = l_ex * alpha + rows_sum4(rx);
         issue(uv + NU);
         u = uv + 1;
     }
