@@ -40,9 +40,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--headline-only", action="store_true",
                    help="only the 60-layer sweep (profiling runs of its kernels)")
-    p.add_argument("--no-flushed", action="store_true",
-                   help="skip the MALL-flushed re-measurement (profiling runs: keeps every decode launch "
-                        "in the kernel trace identical to the timed ones)")
+    p.add_argument("--only", choices=("prefill", "kv_append"),
+                   help="run only this sub-measurement and print it (counter runs of its kernels)")
     p.add_argument("--calib-copy", action="store_true",
                    help="run only a 1 GiB device copy (counter calibration for FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
@@ -603,6 +602,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     digest = kernel_source_digest()
+    if args.only:
+        flush = MallFlush(torch)
+        if args.only == "prefill":
+            sub = prefill_measure(torch, devio, workloads, traffic, flush, {})
+        else:
+            sub = append_measure(torch, devio, workloads, stream, flush)
+        print(json.dumps({"only": args.only, args.only: sub}), flush=True)
+        return
     layers, lays, kv_total, kv_fam = build_sweep(torch, devio, workloads, traffic)
 
     def sweep(global_events=None):

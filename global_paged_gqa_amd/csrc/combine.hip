@@ -62,7 +62,7 @@ __device__ __forceinline__ float uniform(float x) {
 template <int G, int F>  // thread groups; splits a thread has in flight per pass
 __global__ __launch_bounds__(kMaxThreads) void combine_kernel(int num_q_heads, int head_dim, int ns,
                                                               const float *o_part, const float *lse_part,
-                                                              uint16_t *out, float *lse) {
+                                                              uint16_t *out, float *lse, CombineRows rows) {
     constexpr int J = kSums / G;  // partial sums per thread: p, p + G, ...
     static_assert(G * J == kSums && F % J == 0, "sum layout");
     __shared__ f32x4 part[kMaxThreads];  // (G - 1) J C <= 512 for every launch shape
@@ -76,17 +76,34 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(int num_q_heads, i
     const bool owner = d < head_dim;
     const int lane = threadIdx.x & 63;
     const float *op = o_part + bh * ns * head_dim + (owner ? d : 0);
+    // Slots [0, n_live) may be non-empty. For a decode's partials: the splits from the one holding
+    // the row's first visible key to the one holding its last (a row outside [1, max_ctx] fails
+    // its splits with NaN, which the statistics over all slots below catch). Outputs are read
+    // for those slots only; the skipped ones hold lse = -inf and would add nothing.
+    int n_live = ns;
+    if (rows.ctx_lens) {
+        const int L = rows.ctx_lens[b];
+        if (L >= 1 && L <= rows.max_ctx) {
+            const int lo = rows.is_global ? 0 : max(0, L - rows.window);
+            n_live = min(ns, (L - 1) / rows.split_tokens - lo / rows.split_tokens + 1);
+        }
+    }
 
-    // this thread's splits s = base + grp + G k (k < F) of a pass, loads issued up front;
-    // indices past the last slot are clamped to it and their values ignored
+    // this thread's splits s = base + grp + G k (k < F) of a pass, loads issued up front (none
+    // past the live slots: the branch is uniform over the wave)
     float lv[F];
     f32x4 ov[F];
     auto load_pass = [&](int base) {
 #pragma unroll
         for (int k = 0; k < F; ++k) {
-            const int s = min(base + grp + G * k, ns - 1);
-            lv[k] = lp[s];
-            ov[k] = *(const f32x4 *)(op + (int64_t)s * head_dim);
+            if (base + grp + G * k < n_live) {
+                const int s = base + grp + G * k;
+                lv[k] = lp[s];
+                ov[k] = *(const f32x4 *)(op + (int64_t)s * head_dim);
+            } else {
+                lv[k] = -INFINITY;
+                ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     };
     load_pass(0);
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(int num_q_heads, i
     for (int base = 0;;) {
 #pragma unroll
         for (int k = 0; k < F; ++k) {
-            const bool live = base + grp + G * k < ns && lv[k] != -INFINITY;
+            const bool live = base + grp + G * k < n_live && lv[k] != -INFINITY;
             const float w = __expf(lv[k] - LSE);
             // one explicit fma per element, the same in every instantiation
 #pragma unroll
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(int num_q_heads, i
                 acc[k % J][i] = live ? __builtin_fmaf(w, ov[k][i], acc[k % J][i]) : acc[k % J][i];
         }
         base += G * F;
-        if (base >= ns)
+        if (base >= n_live)
             break;
         load_pass(base);
     }
@@ -160,7 +177,8 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(int num_q_heads, i
 }  // namespace
 
 hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
-                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream) {
+                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream,
+                          const CombineRows &rows) {
     const dim3 grid(num_q_heads, batch);
     // one thread per four dims in each group, rounded up to whole waves (head_dim <= 1024);
     // groups and loads in flight by slot count: (1, 4), (1, 8), (2, 8), (2, 16), (4, 16)
@@ -171,7 +189,8 @@ hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_spli
     g = g < max_g ? g : max_g;
     const int f = ns <= 4 * g ? 4 : ns <= 8 * g ? 8 : 16;
     int hq = num_q_heads, hd = head_dim, nsp = num_splits;
-    void *args[] = {&hq, &hd, &nsp, (void *)&o_part, (void *)&lse_part, (void *)&out, (void *)&lse};
+    CombineRows r = rows;
+    void *args[] = {&hq, &hd, &nsp, (void *)&o_part, (void *)&lse_part, (void *)&out, (void *)&lse, &r};
     const void *k = nullptr;
     if (g == 1)
         k = f == 4 ? (const void *)combine_kernel<1, 4> : f == 8 ? (const void *)combine_kernel<1, 8>

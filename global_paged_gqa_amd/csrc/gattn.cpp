@@ -211,8 +211,14 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
     if (e != hipSuccess)
         return GATTN_ERR_HIP;
     if (plan.n_slots > 1) {
+        gattn::CombineRows rows;
+        rows.ctx_lens = ctx_lens;
+        rows.split_tokens = plan.split_tokens;
+        rows.is_global = layer->family == GATTN_GLOBAL;
+        rows.window = layer->window;
+        rows.max_ctx = max_ctx;
         if (gattn::launch_combine(batch, layer->num_q_heads, layer->head_dim, plan.n_slots, a.o_part,
-                                  a.lse_part, out, lse, s) != hipSuccess)
+                                  a.lse_part, out, lse, s, rows) != hipSuccess)
             return GATTN_ERR_HIP;
     }
     return GATTN_OK;

@@ -69,8 +69,16 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared
 hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                    hipStream_t stream);
 
+// Which split slots of a row a decode filled (those past its last key hold lse = -inf): with it the
+// merge reads only those outputs. ctx_lens null: every slot may be non-empty.
+struct CombineRows {
+    const int32_t *ctx_lens = nullptr;
+    int split_tokens = 0, is_global = 1, window = 0, max_ctx = 0;
+};
+
 hipError_t launch_combine(int batch, int num_q_heads, int head_dim, int num_splits, const float *o_part,
-                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
+                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream,
+                          const CombineRows &rows = CombineRows());
 
 hipError_t launch_prefill(const PrefillArgs &a, int head_dim, bool kv_shared, int batch,
                           hipStream_t stream);
