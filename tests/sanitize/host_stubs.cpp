@@ -9,7 +9,8 @@ namespace gattn {
 hipError_t launch_kv_append(const AppendArgs &, int, int, bool, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_split(const DecodeArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_split_fp8(const DecodeArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_combine(int, int, int, int, const float *, const float *, uint16_t *, float *, hipStream_t) {
+hipError_t launch_combine(int, int, int, int, const float *, const float *, uint16_t *, float *, hipStream_t,
+                          const CombineRows &) {
     return hipErrorInvalidValue;
 }
 hipError_t launch_prefill(const PrefillArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
