@@ -11,6 +11,8 @@ namespace {
 
 constexpr int kMaxGroup = 16;
 
+constexpr int kMaxPrefillQHeads = 16384;
+
 int check_layer(const gattn_layer *l) {
     if (!l)
         return GATTN_ERR_NULL_PTR;
@@ -259,6 +261,10 @@ int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k
         return rc;
     if (batch < 0 || max_q < 0 || pt_stride < 1 || num_pages < 1)
         return GATTN_ERR_BAD_SHAPE;
+    // a query tile's rows span at most 256 positions x num_q_heads x head_dim bf16, addressed with
+    // 32-bit offsets
+    if (layer->num_q_heads > kMaxPrefillQHeads)
+        return GATTN_ERR_UNSUPPORTED;
     if (!q || !k_pool || !page_table || !cu_q || !ctx_lens || !out || !lse)
         return GATTN_ERR_NULL_PTR;
     if (layer->kv_shared) {

@@ -324,18 +324,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < RT; ++r)
         p_own[r] = p_first + pos_own(r);
 
-    // ---- Q^T as the B operand: lane holds row n32, dims 16 s + 8 h .. +7 (zeros for padding rows)
+    // ---- Q^T as the B operand: lane holds row n32, dims 16 s + 8 h .. +7 (zeros for padding rows).
+    // The tile's Q rows are first copied into the ring (still unused) with whole 1 KB loads, row m
+    // at m * HD * 2 bytes with its 16-byte chunk c at slot c ^ (m & 31) (a read of 32 rows at one
+    // chunk then touches 32 slots), and read into registers after the copy has landed. Loading
+    // them straight into registers gathered 32 bytes per row and instruction; every workgroup
+    // starts with this load, so it runs while every CU is loading. Rows past the tile's queries
+    // lie beyond the buffer range and load zeros.
     u32x4 qb[RT][NKS];
+    {
+        constexpr int CPRQ = HD / 8;                           // 16-byte chunks per Q row
+        constexpr int QLPW = kRows * CPRQ / 64 / kWaves;       // 1 KB loads per wave
+        const uint16_t *qbase = a.q + ((int64_t)(q0 + tile_q) * Hq + kvh * g) * HD;
+        const uint32_t qbytes = (uint32_t)(((int64_t)(nq - 1) * Hq + g) * HD * 2);
+        const u32x4 qrs = raw_rsrc(qbase, qbytes);
+        const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const uint16_t *qp =
-            a.q + ((int64_t)(q0 + tile_q + (ok_own(r) ? pos_own(r) : 0)) * Hq + kvh * g + m_own(r) % g) * HD + 8 * h;
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            const u32x4 v = *(const u32x4 *)(qp + 16 * s);
-            qb[r][s] = ok_own(r) ? v : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < QLPW; ++i) {
+            const int I = i * kWaves + wave;  // instruction: chunk positions 64 I .. 64 I + 63
+            const int P = 64 * I + lane;
+            const int m = P / CPRQ, c = (P % CPRQ) ^ (m & 31);
+            const int pos = m / g, hq = m - pos * g;
+            ring_load16(qrs, ring_lds + 1024u * (uint32_t)I,
+                        (uint32_t)((((int64_t)pos * Hq + hq) * HD + c * 8) * 2));
         }
     }
+    auto q_from_lds = [&]() {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int m = m_own(r);
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                qb[r][s] = *(const u32x4 *)(ring + m * HD * 2 + (((2 * s + h) ^ (m & 31)) * 16));
+        }
+    };
 
     // O^T tiles of this wave's rows over the whole head dimension (AGPRs)
     f32x16 acc[RT][NDT];
@@ -661,8 +683,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto no_hook = [](int) {};
 
     // Q and the first page ids are in registers before the ring starts, so that inside the
-    // block loop the only vector-memory operations in flight are the ring's own loads.
+    // block loop the only vector-memory operations in flight are the ring's own loads: Q's copy
+    // lands in the ring for every wave, each wave reads its rows, and the ring is free again.
     __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    q_from_lds();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     // Separate pools: units 0..3 (K0, K1, V0, K2) before the loop; iteration j then issues the V
     // of block j+1 (unit 2j+4) after its first barrier and the K of block j+3 (unit 2j+5) after
     // the second, so a K unit is loaded two blocks ahead of its scores and a V unit one block

@@ -221,6 +221,8 @@ int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_
  *   max_q      host-side upper bound of every row's q_len (sets the grid).
  *   out        [total_q][num_q_heads][head_dim] bf16.
  *   lse        [total_q][num_q_heads] fp32, natural log.
+ * num_q_heads above 16384 returns GATTN_ERR_UNSUPPORTED (a query tile's span of
+ * q is addressed with 32-bit offsets).
  * Fail closed on device-side data (pegainfer "[Model] Gemma 4 M3 31B", Proposed
  * Plan: what is not served fails closed): a row whose q_len exceeds max_q or
  * ctx_lens[r], or whose context runs past the page table, gets NaN O and LSE for

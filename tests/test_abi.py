@@ -201,6 +201,8 @@ def test_prefill_and_combine_reject_bad_arguments():
     assert st(g.gattn_prefill, lay, **dict(ok, cu_q=None)) == nat.ERR_NULL_PTR
     assert st(g.gattn_prefill, lay, **dict(ok, max_q=-1)) == nat.ERR_BAD_SHAPE
     assert st(g.gattn_prefill, g.make_layer("local", 32, 16, 256, window=-5), **ok) == nat.ERR_BAD_SHAPE
+    # a query tile's span of q must stay within 32-bit offsets: at most 16384 query heads
+    assert st(g.gattn_prefill, g.make_layer("global", 32768, 2048, 512), **ok) == nat.ERR_UNSUPPORTED
     assert st(g.gattn_combine, 4, 32, 512, 0, 1, 2, 3, 4) == nat.ERR_BAD_SHAPE
     assert st(g.gattn_combine, 4, 32, 510, 3, 1, 2, 3, 4) == nat.ERR_UNSUPPORTED
     assert st(g.gattn_combine, 4, 32, 512, 3, None, 2, 3, 4) == nat.ERR_NULL_PTR
