@@ -25,29 +25,30 @@ constexpr int kThreads = 256;
 constexpr int kTok = 8;     // tokens per workgroup
 constexpr int kUnroll = 4;  // rows a lane loads before it stores them (loads in flight)
 
-// E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits) of the fp32 quotient x / scale
-// (scale > 0): nearest, ties to even, saturating at 448; the sign is x's (a NaN keeps it too).
-__device__ __forceinline__ uint32_t e4m3_code(float x, float scale) {
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
-    const uint32_t a = __builtin_bit_cast(uint32_t, x / scale) & 0x7fffffffu;
-    if (a > 0x7f800000u)  // NaN
-        return sign | 0x7fu;
-    if (a >= 0x43e00000u)  // |quotient| >= 448, infinities included
-        return sign | 0x7eu;
-    if (a < 0x3c800000u)  // below 2^-6: subnormal steps of 2^-9; the scaling by 2^9 is exact
-        return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
-    const uint32_t mant = a & 0x7fffffu;
-    uint32_t code = (((a >> 23) - 120u) << 3) | (mant >> 20);  // exponent rebiased 127 -> 7
-    const uint32_t rest = mant & 0xfffffu;                      // the 20 bits rounded away
-    if (rest > 0x80000u || (rest == 0x80000u && (code & 1u)))
-        ++code;  // a carry into the exponent is the correct next binade; below 448 code stays <= 0x7e
-    return sign | code;
-}
+// Four bf16 values (two packed words) -> four E4M3 bytes of value / scale, first value lowest:
+// the code nearest to the fp32 quotient (IEEE division), ties to the even code, magnitudes of 448
+// and above (infinities included) saturating to 448, a NaN value giving sign | 0x7f. The quotients
+// are clamped to [-448, 448] and converted by the gfx950 conversion instruction (round to
+// nearest even, subnormal codes included, sign of zeros kept); it writes every NaN as 0xff, and a
+// NaN reaches it clamped anyway, so NaN bytes are set afterwards, on the rare waves that hold one.
+// Checked against the oracle's encoder on every bf16 value.
+__device__ __forceinline__ float e4m3_arg(float x, float scale) { return fminf(fmaxf(x / scale, -448.0f), 448.0f); }
 
-// Four bf16 values (two packed words) -> four E4M3 bytes of value / scale, first value lowest.
 __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float scale) {
-    return e4m3_code(bf16_lo(w0), scale) | (e4m3_code(bf16_hi(w0), scale) << 8) |
-           (e4m3_code(bf16_lo(w1), scale) << 16) | (e4m3_code(bf16_hi(w1), scale) << 24);
+    const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_arg(x[0], scale), e4m3_arg(x[1], scale), 0,
+                                                                   false);
+    uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_arg(x[2], scale), e4m3_arg(x[3], scale),
+                                                              (int)lo, true);
+    const bool any_nan = (x[0] != x[0]) | (x[1] != x[1]) | (x[2] != x[2]) | (x[3] != x[3]);
+    if (__builtin_amdgcn_ballot_w64(any_nan)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (x[i] != x[i])
+                code = (code & ~(0xffu << (8 * i))) |
+                       (((__builtin_bit_cast(uint32_t, x[i]) >> 24 & 0x80u) | 0x7fu) << (8 * i));
+    }
+    return code;
 }
 
 template <int HD, bool F8>
