@@ -557,10 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     };
     auto sm_step = [&](int step, SmState &z, f32x16 &st, u32x4 (&pf)[2], float &alpha, int r) {
         if (step < 4) {
-            // scaled in place on every block; on edge blocks the invisible keys then become -inf
-#pragma unroll
-            for (int v = 4 * step; v < 4 * step + 4; ++v)
-                st[v] *= scale;
+            // raw scores: the scale enters the exponent (step 5-8) and the row maximum (step 4);
+            // on edge blocks the invisible keys become -inf
             if (!z.interior) {
 #pragma unroll
                 for (int v = 4 * step; v < 4 * step + 4; ++v)
@@ -570,7 +568,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             for (int v = 4 * step; v < 4 * step + 4; ++v)
                 z.mx = fmaxf(z.mx, st[v]);
         } else if (step == 4) {
-            const float m_new = fmaxf(m_run[r], halves_max(z.mx));
+            // the scale is positive and rounding is monotonic: scale * max(raw) is the maximum of the
+            // rounded scaled scores, exactly
+            const float m_new = fmaxf(m_run[r], halves_max(z.mx) * scale);
             const bool resc = m_new > m_run[r] + kRescaleLog2;
             // While the reference is still -inf every weight so far was exactly 0, so the
             // accumulators and sums are zero: they need no rescale (alpha 1 leaves the same bits
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         } else if (step < 9) {
 #pragma unroll
             for (int v = 4 * (step - 5); v < 4 * (step - 5) + 4; ++v)
-                st[v] = fast_exp2(st[v] - z.mb);  // the weights replace the scores
+                st[v] = fast_exp2(__builtin_fmaf(st[v], scale, -z.mb));  // the weights replace the scores
         } else if (step < 11) {
             const int q = step - 9;
             pf[q] = u32x4{pack_bf16x2(st[8 * q + 0], st[8 * q + 1]), pack_bf16x2(st[8 * q + 2], st[8 * q + 3]),
