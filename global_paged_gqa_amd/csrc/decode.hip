@@ -59,11 +59,12 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
 }
 
-template <int HD, bool SHARED, int W, int DS, int kSliceBytes, bool F8 = false>
-__global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a) {
+template <int HD, bool SHARED, int W, int DS, int kSliceBytes, bool F8 = false, int NS = 1>
+__global__ __launch_bounds__(NS * W * DS * 64) void decode_split_kernel(DecodeArgs a) {
     // W page streams of DS waves each; a wave streams its share of the head dims of its
-    // stream's pages through its own kSliceBytes of LDS
-    constexpr int kWaves = W * DS;
+    // stream's pages through its own kSliceBytes of LDS. NS > 1: the workgroup takes all NS split
+    // slots of its (row, KV head), one group of W * DS waves per slot, and merges them itself.
+    constexpr int kWaves = NS * W * DS;
     constexpr int kThreads = kWaves * 64;
     constexpr int kRingBytes = kWaves * kSliceBytes;
     constexpr int NKS = HD / 32 / DS;            // K-steps of 32 dims in the wave's score partial
@@ -89,20 +90,24 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     static_assert(NU * LPU + 1 <= 63, "vmcnt range");
     static_assert(16 * HD * 4 <= DS * kSliceBytes, "merge buffer");
     static_assert(!F8 || DS == 1, "fp8 pools: whole head dims per wave");
+    static_assert(NS == 1 || DS == 1, "merged slots: whole head dims per wave");
+    static_assert(NS * W * 16 * HD * 4 <= kRingBytes, "merge buffer (merged slots)");
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
-    __shared__ float sm_m[W][16];
-    __shared__ float sm_l[W][16];   // row sums of the bf16 weights (normalise O)
-    __shared__ float sm_lx[W][16];  // row sums of the fp32 weights (LSE)
-    __shared__ int sm_bad[W];
+    __shared__ float sm_m[NS][W][16];
+    __shared__ float sm_l[NS][W][16];   // row sums of the bf16 weights (normalise O)
+    __shared__ float sm_lx[NS][W][16];  // row sums of the fp32 weights (LSE)
+    __shared__ int sm_bad[NS][W];
     __shared__ f32x4 sm_part[2][DS][64];  // score partials of the dim-split waves (double buffer)
+    __shared__ float sm_lse[NS][16];      // merged slots: each slot's LSE per head
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int pw = wave / DS, dq = wave % DS;  // page stream, head-dim segment
+    const int grp = wave / (W * DS);                            // split slot within the workgroup
+    const int pw = (wave % (W * DS)) / DS, dq = wave % DS;      // page stream, head-dim segment
     const int c16 = lane & 15;  // MFMA row/column index of this lane
     const int r4 = lane >> 4;   // 16-lane row of this lane
-    const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int slot = NS > 1 ? grp : (int)blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int g = a.group;
     const int Hq = a.num_q_heads;
 
@@ -119,13 +124,20 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
         te = (int)min<int64_t>(L, (s_abs + 1) * S);
     }
     const bool direct = a.n_slots == 1;
-    if (!bad_len && tb >= te) {  // split outside the visible range: mark it empty
-        if (threadIdx.x < g)
-            a.lse_part[((int64_t)b * Hq + kvh * g + threadIdx.x) * a.n_slots + slot] = -INFINITY;
-        return;
+    // A split outside the visible range is empty. On its own it marks its slot and ends; as a
+    // slot of a merging workgroup its waves stream nothing and still reach every barrier, and the
+    // merge below gives it lse = -inf, which the final merge skips.
+    const bool empty = !bad_len && tb >= te;
+    if constexpr (NS == 1) {
+        if (empty) {
+            if (threadIdx.x < g)
+                a.lse_part[((int64_t)b * Hq + kvh * g + threadIdx.x) * a.n_slots + slot] = -INFINITY;
+            return;
+        }
     }
-    const int pg0 = tb / kPage;
-    const int npg = bad_len ? 0 : (te - 1) / kPage - pg0 + 1;
+    // (an empty slot's tb may lie past the row's last table entry: it reads entry 0 instead)
+    const int pg0 = bad_len || empty ? 0 : tb / kPage;
+    const int npg = bad_len || empty ? 0 : (te - 1) / kPage - pg0 + 1;
     const int my_pages = npg > pw ? (npg - pw + W - 1) / W : 0;  // this stream's: w, w+W, ...
     const int32_t *pt = a.page_table + (int64_t)b * a.pt_stride;
     const int pg_hi = npg > 0 ? pg0 + npg - 1 : pg0;  // last table entry this workgroup may read
@@ -374,24 +386,25 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
     // and each contributes its head dims.
     const bool wave_bad = __builtin_amdgcn_ballot_w64(bad_page) != 0;
     if (lane == 0 && dq == 0)
-        sm_bad[pw] = wave_bad;
+        sm_bad[grp][pw] = wave_bad;
     if (r4 == 0 && dq == 0) {
-        sm_m[pw][c16] = m_run;
-        sm_l[pw][c16] = l_run;
-        sm_lx[pw][c16] = l_ex;
+        sm_m[grp][pw][c16] = m_run;
+        sm_l[grp][pw][c16] = l_run;
+        sm_lx[grp][pw][c16] = l_ex;
     }
     __syncthreads();  // every wave is done with its slice; the states are visible
-    float *const mo = (float *)ring;  // [W][g][HD] fp32, each stream's acc scaled to the common max
+    // [NS][W][g][HD] fp32, each stream's acc scaled to its slot's common max
+    float *const mo = (float *)ring;
     {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w)
-            M = fmaxf(M, sm_m[w][c16]);
+            M = fmaxf(M, sm_m[grp][w][c16]);
         const float cw = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
         if (c16 < g) {
             if constexpr (F8) {
                 // tiles 2T and 2T + 1 interleave: element i of each is dim 32 T + 8 r4 + 2 i (+ 1)
-                float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 8 * r4;
+                float *dst = mo + (((size_t)grp * W + pw) * g + c16) * HD + SEG * dq + 8 * r4;
 #pragma unroll
                 for (int T = 0; T < NDT / 2; ++T) {
                     const f32x4 e = acc[2 * T] * cw, o = acc[2 * T + 1] * cw;
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
                     *(f32x4 *)(dst + 32 * T + 4) = f32x4{e[2], o[2], e[3], o[3]};
                 }
             } else {
-                float *dst = mo + ((size_t)pw * g + c16) * HD + SEG * dq + 4 * r4;
+                float *dst = mo + (((size_t)grp * W + pw) * g + c16) * HD + SEG * dq + 4 * r4;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
                     *(f32x4 *)(dst + 16 * dt) = acc[dt] * cw;
@@ -407,25 +420,28 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
         }
     }
     __syncthreads();
+    // each slot's result: element e of slot sl by one thread
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
     bool bad = bad_len;
 #pragma unroll
     for (int w = 0; w < W; ++w)
-        bad = bad || sm_bad[w];
+        bad = bad || sm_bad[sl][w];
     for (int e = threadIdx.x * 4; e < g * HD; e += kThreads * 4) {
         const int hn = e / HD, d = e % HD;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w)
-            M = fmaxf(M, sm_m[w][hn]);
+            M = fmaxf(M, sm_m[sl][w][hn]);
         float lsum = 0.f, lxsum = 0.f;
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float mw = sm_m[w][hn];
+            const float mw = sm_m[sl][w][hn];
             const float cw = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-            lsum += cw * sm_l[w][hn];
-            lxsum += cw * sm_lx[w][hn];
-            o += *(const f32x4 *)(mo + ((size_t)w * g + hn) * HD + d);
+            lsum += cw * sm_l[sl][w][hn];
+            lxsum += cw * sm_lx[sl][w][hn];
+            o += *(const f32x4 *)(mo + (((size_t)sl * W + w) * g + hn) * HD + d);
         }
         const float inv = F8 ? a.v_scale / lsum : 1.0f / lsum;
         float lse = (M + fast_log2(lxsum)) * kLn2;
@@ -435,7 +451,12 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
         if (bad)
             lse = __builtin_nanf("");
         const int64_t bh = (int64_t)b * Hq + kvh * g + hn;
-        if (direct) {
+        if constexpr (NS > 1) {
+            // kept for the merge (in the slot's first stream buffer: this thread read it last)
+            *(f32x4 *)(mo + ((size_t)sl * W * g + hn) * HD + d) = o;
+            if (d == 0)
+                sm_lse[sl][hn] = lse;
+        } else if (direct) {
             *(u32x2 *)(a.out + bh * HD + d) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             if (d == 0)
                 a.lse[bh] = lse;
@@ -443,6 +464,57 @@ __global__ __launch_bounds__(W * DS * 64) void decode_split_kernel(DecodeArgs a)
             *(f32x4 *)(a.o_part + (bh * a.n_slots + slot) * HD + d) = o;
             if (d == 0)
                 a.lse_part[bh * a.n_slots + slot] = lse;
+        }
+    }
+    }  // slots
+    if constexpr (NS > 1) {
+        // The slots merged with the arithmetic of the separate merge (combine.hip) on the same
+        // values, so the bits match it: M the largest slot LSE (NaN propagates); the exp-sum as
+        // (e0 + e1) + (e2 + e3); LSE = M + ln(sum); O = ((a0 + a1) + a2) + a3 with a_s = w_s o_s
+        // by one fma; empty slots (lse = -inf) add zeros.
+        static_assert(NS <= 4, "merged slots: the fixed four-sum order");
+        __syncthreads();
+        for (int e = threadIdx.x * 4; e < g * HD; e += kThreads * 4) {
+            const int hn = e / HD, d = e % HD;
+            float ls[4], M = -INFINITY;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                ls[s2] = s2 < NS ? sm_lse[s2][hn] : -INFINITY;
+                M = nan_max(M, ls[s2]);
+            }
+            const int64_t bh = (int64_t)b * Hq + kvh * g + hn;
+            if (M == -INFINITY) {  // every slot empty
+                *(u32x2 *)(a.out + bh * HD + d) = u32x2{0u, 0u};
+                if (d == 0)
+                    a.lse[bh] = -INFINITY;
+                continue;
+            }
+            float ex[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                ex[s2] = ls[s2] == -INFINITY ? 0.f : __expf(ls[s2] - M);
+            const float LSE = M + __logf((ex[0] + ex[1]) + (ex[2] + ex[3]));
+            f32x4 part[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                part[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (s2 < NS && ls[s2] != -INFINITY) {
+                    const float w = __expf(ls[s2] - LSE);
+                    const f32x4 os = *(const f32x4 *)(mo + ((size_t)s2 * W * g + hn) * HD + d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part[s2][i] = __builtin_fmaf(w, os[i], 0.f);
+                }
+            }
+            f32x4 o = part[0];
+#pragma unroll
+            for (int s2 = 1; s2 < 4; ++s2)
+                o += part[s2];
+            if (M != M)
+                o = f32x4{M, M, M, M};
+            *(u32x2 *)(a.out + bh * HD + d) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            if (d == 0)
+                a.lse[bh] = LSE;
         }
     }
 }
@@ -476,6 +548,18 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
     constexpr int W = DecodeShape<HD>::waves;
     constexpr int SLICE = DecodeShape<HD>::slice;
     void *args[] = {(void *)&a};
+    if constexpr (HD == 256) {
+        // two or three slots per row (a local row's window over its splits): one workgroup per
+        // (row, KV head) runs them all and merges them, in place of the separate merge launch
+        if (decode_merges_slots(HD, false, a.n_slots)) {
+            const dim3 rows(1, grid.y, grid.z);
+            if (a.n_slots == 2)
+                return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, 1, SLICE, false, 2>, rows,
+                                       dim3(2 * W * 64), args, 0, stream);
+            return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, W, 1, SLICE, false, 3>, rows,
+                                   dim3(3 * W * 64), args, 0, stream);
+        }
+    }
     if constexpr (HD == 512) {
         const int64_t items = (int64_t)grid.x * grid.y * grid.z;
         if (items <= kNumCUs)
@@ -490,6 +574,10 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool decode_merges_slots(int head_dim, bool fp8, int n_slots) {
+    return head_dim == 256 && !fp8 && n_slots >= 2 && n_slots <= 3;
+}
 
 // FP8 pools at head_dim 256 (4 KB units): two page streams of one wave with four units (two pages)
 // each. A workgroup then holds 32 KB of LDS and the wave's registers allow two waves per SIMD, so

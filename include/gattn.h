@@ -155,7 +155,10 @@ size_t gattn_decode_workspace_bytes(const gattn_layer *layer, int batch, int max
  *   out        [batch][num_q_heads][head_dim] bf16.
  *   lse        [batch][num_q_heads] fp32, natural log.
  * Enqueues the split kernel, then (when a row can have several splits) the
- * combine kernel, on `stream`.
+ * combine kernel, on `stream`; at head_dim 256 with bf16 pools and two or three
+ * split slots per row (a local row's window over 512-token splits, say) one
+ * kernel runs all of a row's slots and merges them with the combine's arithmetic,
+ * with the same bits. The workspace size is the same either way.
  */
 int gattn_decode(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
                  const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,

@@ -75,6 +75,19 @@ def test_local_decode_small(devio, split):
     check(b, out, lse, tag=f"local small S={split}")
 
 
+@pytest.mark.parametrize("split", [512, 256])
+def test_local_rows_ending_on_a_split_boundary(devio, split):
+    """Local rows whose context ends exactly on a split boundary, in a page table exactly as wide
+    as the longest row: a row's last split slot is then empty and starts past the row's last table
+    entry (the workgroup that merges a row's slots must not read that entry), beside rows whose
+    windows are cut by the splits elsewhere."""
+    L = np.array([2048, 1536, 2048, 1000, 2048], np.int32)
+    b = workloads.make_batch(workloads.LOCAL_31B, L, np.ones(len(L), np.int32), (61, split), back="all")
+    assert b.pt_stride == 2048 // 16
+    out, lse = devio.decode(b, split)
+    check(b, out, lse, tag=f"split-boundary rows S={split}")
+
+
 def test_cfg3_local_decode_full(devio):
     b = workloads.cfg3_local_decode()
     out, lse = devio.decode(b, 512)
