@@ -212,7 +212,8 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
                              : gattn::launch_decode_split(a, layer->head_dim, layer->kv_shared != 0, batch, s);
     if (e != hipSuccess)
         return GATTN_ERR_HIP;
-    if (plan.n_slots > 1 && !gattn::decode_merges_slots(layer->head_dim, fp8, plan.n_slots)) {
+    if (plan.n_slots > 1 &&
+        !gattn::decode_merges_slots(layer->head_dim, fp8, plan.n_slots, (int64_t)batch * layer->num_kv_heads)) {
         gattn::CombineRows rows;
         rows.ctx_lens = ctx_lens;
         rows.split_tokens = plan.split_tokens;

@@ -66,9 +66,10 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared
                                hipStream_t stream);
 
 // Decode over E4M3 pools (head_dim 256 with separate K and V pools, or head_dim 512).
-// Whether the decode launch for this shape merges a row's split slots itself (bf16 pools,
-// head_dim 256, two or three slots), so that no separate merge follows.
-bool decode_merges_slots(int head_dim, bool fp8, int n_slots);
+// Whether the decode launch for this shape merges a row's split slots itself (head_dim 256,
+// two or three slots; FP8 pools only for at most one (row, KV head) per CU), so that no
+// separate merge follows.
+bool decode_merges_slots(int head_dim, bool fp8, int n_slots, int64_t rows_x_kv_heads);
 
 hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                    hipStream_t stream);

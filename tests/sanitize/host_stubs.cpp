@@ -14,7 +14,7 @@ hipError_t launch_combine(int, int, int, int, const float *, const float *, uint
     return hipErrorInvalidValue;
 }
 hipError_t launch_prefill(const PrefillArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
-bool decode_merges_slots(int, bool, int) { return false; }
+bool decode_merges_slots(int, bool, int, int64_t) { return false; }
 hipError_t noalloc_scratch(void **, size_t *) { return hipErrorInvalidValue; }
 
 }  // namespace gattn
