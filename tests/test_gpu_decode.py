@@ -172,10 +172,10 @@ def test_bitwise_batch_invariance_and_reorder(devio):
 
 
 @pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "global-kv-shared"])
-def test_bitwise_dims_split_invariance(devio, spec):
-    """A head_dim 512 grid of at most 256 (row, KV head, split) items runs four waves per item,
-    each on a quarter of the head dims, with 32 KB of LDS each; up to 512 items the same with
-    16 KB each; a larger grid runs one wave per item. A row gives the same bits in every shape:
+def test_bitwise_launch_shape_invariance(devio, spec):
+    """A head_dim 512 grid of at most 256 (row, KV head, split) items runs a split's four page
+    streams on four waves, one each; up to 512 items on two waves of two streams; a larger grid
+    on one wave that runs the four in turn. A row gives the same bits in every shape:
     alone, in 2- and 4-row batches (16 x 4 x 4 = 256 items at most), in a 6-row batch (384 items)
     and inside a 10-row batch (640 items). The small-grid results also match the oracle."""
     L = workloads.ragged((14, int(spec.kv_shared)), 1, 8192, 10)
@@ -187,6 +187,23 @@ def test_bitwise_dims_split_invariance(devio, spec):
         o, l = _run(devio, sub, 512, max_ctx=8192)
         assert np.array_equal(o, o_all[rows]) and np.array_equal(l, l_all[rows]), rows
     check(sub, o, l, tag=f"{spec.family} kv_shared={spec.kv_shared} small grid")
+
+
+
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "global-kv-shared"])
+def test_page_stream_edges(devio, spec):
+    """Splits of 128 keys (eight pages, two per page stream at head_dim 512) with every page count
+    from one to eight in the last split, so that one, two or three of the four streams are empty or
+    one page short, and a poisoned (NaN) pool behind every unused slot. Each row alone runs the
+    four-wave shape (256 items), two rows the two-wave shape, all thirteen the one-wave shape; every
+    row gives the same bits in all three and matches the oracle."""
+    L = np.array([1, 16, 17, 33, 49, 64, 65, 90, 100, 113, 128, 8192 - 7, 8192], np.int32)
+    b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (17, int(spec.kv_shared)), back="all", poison=True)
+    o_all, l_all = _run(devio, b, 128, max_ctx=8192)
+    check(b, o_all, l_all, tag=f"{spec.family} kv_shared={spec.kv_shared} stream edges")
+    for rows in ([0], [4], [7], [12], [2, 9], [11, 5]):
+        o, l = _run(devio, b.subset(rows), 128, max_ctx=8192)
+        assert np.array_equal(o, o_all[rows]) and np.array_equal(l, l_all[rows]), rows
 
 
 # ------------------------------------------------------------------------ index probes
@@ -318,7 +335,7 @@ def test_combine_bits_independent_of_slot_count(devio, n, hd):
 
 # ------------------------------------------------------------------------ head_dim 512 index probes
 PROBE_L = 3000
-PROBE_T = (0, 1, 15, 16, 511, 512, 1023, 1024, 1025, 2047, 2048, 2559, 2560, PROBE_L - 17, PROBE_L - 16,
+PROBE_T = (0, 1, 15, 16, 32, 48, 64, 511, 512, 1023, 1024, 1025, 2047, 2048, 2559, 2560, PROBE_L - 17, PROBE_L - 16,
            PROBE_L - 1)
 
 
@@ -347,20 +364,21 @@ def _probe_batch(spec, t_star, key, n_filler=0, pt_stride=None, code_of=None):
 
 
 HD512_SHAPES = {  # name: (kv_shared, split, filler rows, max_ctx, pt_stride) -> items = slots * 4 * rows
-    "global-4waves-32k": (False, 512, 0, None, None),        # 6 x 4 = 24 items
-    "global-4waves-16k": (False, 512, 1, 20000, 1250),       # 40 x 4 x 2 = 320 items
+    "global-4waves": (False, 512, 0, None, None),            # 6 x 4 = 24 items
+    "global-2waves": (False, 512, 1, 20000, 1250),           # 40 x 4 x 2 = 320 items
     "global-1wave": (False, 512, 8, 8192, 512),               # 16 x 4 x 9 = 576 items
-    "kv-shared-4waves-32k": (True, 1024, 0, None, None),     # 3 x 4 = 12 items
-    "kv-shared-4waves-16k": (True, 1024, 1, 40000, 2500),    # 40 x 4 x 2 = 320 items
+    "kv-shared-4waves": (True, 1024, 0, None, None),         # 3 x 4 = 12 items
+    "kv-shared-2waves": (True, 1024, 1, 40000, 2500),        # 40 x 4 x 2 = 320 items
     "kv-shared-1wave": (True, 1024, 8, 16384, 1024),         # 16 x 4 x 9 = 576 items
 }
 
 
 @pytest.mark.parametrize("shape", list(HD512_SHAPES))
 def test_position_probe_hd512(devio, shape):
-    """The position probe at head_dim 512 in each launch shape of the global family (one wave per
-    item, or four head-dim waves with 32 KB or 16 KB slices; separate pools and K=V), swept over
-    page, split and shape-relevant edges: the output must be V[t*] bit for bit in every head."""
+    """The position probe at head_dim 512 in each launch shape of the global family (a split's
+    four page streams on four waves, on two waves of two streams, or on one wave in turn; separate
+    pools and K=V), swept over page, split and stream edges: the output must be V[t*] bit for bit
+    in every head."""
     shared, split, n_fill, max_ctx, pt_stride = HD512_SHAPES[shape]
     spec = workloads.LayerSpec("global", 32, 4, 512, kv_shared=shared, scale=1.0)
     for t_star in PROBE_T:
