@@ -27,8 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% bf16 MFMA peak)"
-SWEEP_GLOBAL_KERNEL = "decode_split_kernel<512, true, 1, 1, 32768>"
-CFG2_KERNEL = "decode_split_kernel<512, false, 1, 1, 32768>"
+SWEEP_GLOBAL_KERNEL = "decode_split_kernel<512, true, 1, 32768>"
+CFG2_KERNEL = "decode_split_kernel<512, false, 1, 32768>"
 
 
 def parse():
