@@ -395,20 +395,20 @@ def build_sweep(torch, devio, workloads, traffic):
 
 def combine_time(torch, nat, d, split, stream, n=50):
     """Mean duration of the logsumexp combine alone on the partials a DeviceLayout's last decode left in
-    its workspace (to separate the split kernel's own duration from the whole call)."""
+    its workspace (to separate the split kernel's own duration from the whole call): n combines back to
+    back between one pair of events, so that the events' own latency is not charged to each of them."""
     lay, s = d.lay, d.lay.spec
     ns = d.workspace_bytes(split) // (4 * (s.head_dim + 1) * lay.B * s.num_q_heads)
     n_o = lay.B * s.num_q_heads * ns * s.head_dim
     o_part, lse_part = d.workspace[:n_o], d.workspace[n_o:n_o + lay.B * s.num_q_heads * ns]
-    evs = []
+    nat.gattn_combine(lay.B, s.num_q_heads, s.head_dim, ns, o_part, lse_part, d.out, d.lse, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for _ in range(n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         nat.gattn_combine(lay.B, s.num_q_heads, s.head_dim, ns, o_part, lse_part, d.out, d.lse, stream)
-        e1.record(stream)
-        evs.append((e0, e1))
+    e1.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / n
+    return e0.elapsed_time(e1) * 1e-3 / n
 
 
 def sweep_extras(torch, devio, workloads, traffic, stream, layers, lays, kv_total, kv_fam, t_sweep, reps=10):
@@ -522,16 +522,17 @@ def cfg2_measure(torch, devio, workloads, traffic, stream, flush, digest, steps=
     ns = nat.gattn_decode_workspace_bytes(d.layer, batch.B, int(batch.ctx_lens.max()), 512) // (
         4 * (s.head_dim + 1) * batch.B * s.num_q_heads)
     n_o = batch.B * s.num_q_heads * ns * s.head_dim
-    evs = []
+    # the merge alone, back to back between one pair of events (see combine_time)
+    nat.gattn_combine(batch.B, s.num_q_heads, s.head_dim, ns, d.workspace[:n_o], d.workspace[n_o:], d.out, d.lse,
+                      stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for _ in range(50):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         nat.gattn_combine(batch.B, s.num_q_heads, s.head_dim, ns, d.workspace[:n_o], d.workspace[n_o:], d.out, d.lse,
                           stream)
-        e1.record(stream)
-        evs.append((e0, e1))
+    e1.record(stream)
     torch.cuda.synchronize()
-    tc = sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / len(evs)
+    tc = e0.elapsed_time(e1) * 1e-3 / 50
     return batch, {"workload": "global decode: batch 32, 32 q heads, 4 KV heads, head_dim 512, contexts "
                                "~U{1..8192}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
                    "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
