@@ -102,6 +102,15 @@ _lib.gattn_kv_append_fp8.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_
                                      c_int, c_vp, c_vp, c_int, c_int, c_vp, c_vp]
 _lib.gattn_combine.restype = c_int
 _lib.gattn_combine.argtypes = [c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]
+_lib.gattn_decode_graphs_create.restype = c_int
+_lib.gattn_decode_graphs_create.argtypes = [ctypes.POINTER(Layer), c_vp, c_vp, c_vp, c_i64, c_vp, c_int, c_vp, c_int,
+                                            c_int, c_vp, c_size, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(c_vp)]
+_lib.gattn_decode_graphs_bucket.restype = c_int
+_lib.gattn_decode_graphs_bucket.argtypes = [c_vp, c_int]
+_lib.gattn_decode_graphs_launch.restype = c_int
+_lib.gattn_decode_graphs_launch.argtypes = [c_vp, c_int, c_vp]
+_lib.gattn_decode_graphs_destroy.restype = None
+_lib.gattn_decode_graphs_destroy.argtypes = [c_vp]
 
 
 def _check(rc, where):
@@ -187,10 +196,38 @@ def gattn_combine(batch, num_q_heads, head_dim, num_splits, o_part, lse_part, ou
     _check(rc, "gattn_combine")
 
 
+def gattn_decode_graphs_create(layer, q, k_pool, v_pool, num_pages, page_table, pt_stride, ctx_lens, max_ctx,
+                               split_tokens, workspace, workspace_bytes, out, lse, buckets):
+    """Returns the handle (an int) of the captured set; ``buckets`` is a sequence of batch sizes."""
+    arr = (ctypes.c_int32 * len(buckets))(*[int(b) for b in buckets])
+    handle = c_vp()
+    rc = _lib.gattn_decode_graphs_create(ctypes.byref(layer), _addr(q), _addr(k_pool), _addr(v_pool), int(num_pages),
+                                         _addr(page_table), int(pt_stride), _addr(ctx_lens), int(max_ctx),
+                                         int(split_tokens), _addr(workspace), int(workspace_bytes), _addr(out),
+                                         _addr(lse), arr, len(buckets), ctypes.byref(handle))
+    _check(rc, "gattn_decode_graphs_create")
+    return handle.value
+
+
+def gattn_decode_graphs_bucket(graphs, batch):
+    return _lib.gattn_decode_graphs_bucket(graphs, int(batch))
+
+
+def gattn_decode_graphs_launch(graphs, batch, stream=None):
+    rc = _lib.gattn_decode_graphs_launch(graphs, int(batch), _stream(stream))
+    _check(rc, "gattn_decode_graphs_launch")
+
+
+def gattn_decode_graphs_destroy(graphs):
+    _lib.gattn_decode_graphs_destroy(graphs)
+
+
 def exported_symbols():
     """Names the shared library exports (for the ABI check)."""
     return sorted(n for n in ("gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
                               "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_noalloc",
                               "gattn_decode_fp8kv", "gattn_prefill",
-                              "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8")
+                              "gattn_combine", "gattn_kv_append", "gattn_kv_append_fp8",
+                              "gattn_decode_graphs_create", "gattn_decode_graphs_bucket",
+                              "gattn_decode_graphs_launch", "gattn_decode_graphs_destroy")
                   if hasattr(_lib, n))

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgattn.so")
-SOURCES = ["gattn.cpp", "decode.hip", "combine.hip", "prefill.hip", "append.hip", "noalloc.hip"]
+SOURCES = ["gattn.cpp", "graphs.cpp", "decode.hip", "combine.hip", "prefill.hip", "append.hip", "noalloc.hip"]
 # Per-source extra hipcc flags. Decode: MFMA accumulators in VGPRs. Its softmax rescales the
 # O accumulators with vector multiplies; held in AGPRs, they were copied to VGPRs and back on
 # every page (a quarter of a page's instructions at head_dim 512). The prefill kernels keep

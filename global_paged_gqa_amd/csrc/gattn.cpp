@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <new>
+
 #include "kernels.h"
 
 namespace {
@@ -130,7 +132,8 @@ namespace {
 int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool, const void *v_pool, bool fp8,
                 float k_scale, float v_scale, int64_t num_pages, const int32_t *page_table, int pt_stride,
                 const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
-                size_t workspace_bytes, uint16_t *out, float *lse, void *stream, bool noalloc = false) {
+                size_t workspace_bytes, uint16_t *out, float *lse, void *stream, bool noalloc = false,
+                bool check_only = false) {
     int rc = check_layer(layer);
     if (rc != GATTN_OK)
         return rc;
@@ -175,7 +178,7 @@ int decode_impl(const gattn_layer *layer, const uint16_t *q, const void *k_pool,
         return GATTN_ERR_WORKSPACE_TOO_SMALL;
     if (need > 0 && !workspace)
         return GATTN_ERR_NULL_PTR;
-    if (batch == 0)
+    if (batch == 0 || check_only)
         return GATTN_OK;
 
     gattn::DecodeArgs a{};
@@ -252,6 +255,93 @@ int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_
                        size_t workspace_bytes, uint16_t *out, float *lse, void *stream) {
     return decode_impl(layer, q, k_pool, v_pool, true, k_scale, v_scale, num_pages, page_table, pt_stride, ctx_lens,
                        batch, max_ctx, split_tokens, workspace, workspace_bytes, out, lse, stream);
+}
+
+}  // extern "C"
+
+// The decode graph bucket set: one instantiated graph per bucket size, in increasing order.
+struct gattn_decode_graphs {
+    int n;
+    int32_t buckets[GATTN_MAX_GRAPH_BUCKETS];
+    void *exec[GATTN_MAX_GRAPH_BUCKETS];
+};
+
+extern "C" {
+
+void gattn_decode_graphs_destroy(gattn_decode_graphs *graphs) {
+    if (!graphs)
+        return;
+    for (int i = 0; i < graphs->n; ++i)
+        gattn::graph_free(graphs->exec[i]);
+    delete graphs;
+}
+
+int gattn_decode_graphs_create(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
+                               const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                               const int32_t *ctx_lens, int max_ctx, int split_tokens, void *workspace,
+                               size_t workspace_bytes, uint16_t *out, float *lse, const int32_t *buckets,
+                               int n_buckets, gattn_decode_graphs **graphs) {
+    if (!graphs)
+        return GATTN_ERR_NULL_PTR;
+    *graphs = nullptr;
+    if (!buckets)
+        return GATTN_ERR_NULL_PTR;
+    if (n_buckets < 1 || n_buckets > GATTN_MAX_GRAPH_BUCKETS)
+        return GATTN_ERR_BAD_SHAPE;
+    for (int i = 0; i < n_buckets; ++i)
+        if (buckets[i] < 1 || (i > 0 && buckets[i] <= buckets[i - 1]))
+            return GATTN_ERR_BAD_SHAPE;
+    // every bucket's call is checked before anything is captured
+    for (int i = 0; i < n_buckets; ++i) {
+        const int rc = decode_impl(layer, q, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride,
+                                   ctx_lens, buckets[i], max_ctx, split_tokens, workspace, workspace_bytes, out, lse,
+                                   nullptr, false, true);
+        if (rc != GATTN_OK)
+            return rc;
+    }
+    gattn_decode_graphs *set = new (std::nothrow) gattn_decode_graphs{};
+    if (!set)
+        return GATTN_ERR_HIP;
+    for (int i = 0; i < n_buckets; ++i) {
+        hipStream_t cs = nullptr;
+        if (gattn::graph_capture_begin(&cs) != hipSuccess) {
+            gattn_decode_graphs_destroy(set);
+            return GATTN_ERR_HIP;
+        }
+        const int rc = decode_impl(layer, q, k_pool, v_pool, false, 1.0f, 1.0f, num_pages, page_table, pt_stride,
+                                   ctx_lens, buckets[i], max_ctx, split_tokens, workspace, workspace_bytes, out, lse,
+                                   (void *)cs);
+        void *exec = nullptr;
+        const hipError_t e = gattn::graph_capture_end(cs, &exec);
+        if (rc != GATTN_OK || e != hipSuccess) {
+            gattn::graph_free(exec);
+            gattn_decode_graphs_destroy(set);
+            return rc != GATTN_OK ? rc : GATTN_ERR_HIP;
+        }
+        set->buckets[i] = buckets[i];
+        set->exec[i] = exec;
+        set->n = i + 1;
+    }
+    *graphs = set;
+    return GATTN_OK;
+}
+
+int gattn_decode_graphs_bucket(const gattn_decode_graphs *graphs, int batch) {
+    if (!graphs || batch < 1)
+        return -1;
+    for (int i = 0; i < graphs->n; ++i)
+        if (graphs->buckets[i] >= batch)
+            return graphs->buckets[i];
+    return -1;
+}
+
+int gattn_decode_graphs_launch(const gattn_decode_graphs *graphs, int batch, void *stream) {
+    if (!graphs)
+        return GATTN_ERR_NULL_PTR;
+    for (int i = 0; i < graphs->n; ++i)
+        if (batch >= 1 && graphs->buckets[i] >= batch)
+            return gattn::graph_launch(graphs->exec[i], (hipStream_t)stream) == hipSuccess ? GATTN_OK : GATTN_ERR_HIP;
+    return GATTN_ERR_BAD_SHAPE;
 }
 
 int gattn_prefill(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,

@@ -71,6 +71,14 @@ hipError_t launch_decode_split(const DecodeArgs &a, int head_dim, bool kv_shared
 // separate merge follows.
 bool decode_merges_slots(int head_dim, bool fp8, int n_slots, int64_t rows_x_kv_heads);
 
+// Decode graph capture (graphs.cpp): begin capturing on a new private stream of the current device;
+// end the capture into an instantiated graph (*exec, NULL on failure) and free the stream; launch
+// and free an instantiated graph.
+hipError_t graph_capture_begin(hipStream_t *s);
+hipError_t graph_capture_end(hipStream_t s, void **exec);
+hipError_t graph_launch(void *exec, hipStream_t s);
+void graph_free(void *exec);
+
 hipError_t launch_decode_split_fp8(const DecodeArgs &a, int head_dim, bool kv_shared, int batch,
                                    hipStream_t stream);
 

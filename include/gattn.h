@@ -210,6 +210,61 @@ int gattn_decode_fp8kv(const gattn_layer *layer, const uint16_t *q, const uint8_
                        const int32_t *ctx_lens, int batch, int max_ctx, int split_tokens, void *workspace,
                        size_t workspace_bytes, uint16_t *out, float *lse, void *stream);
 
+/* Most bucket sizes one decode graph set holds. */
+#define GATTN_MAX_GRAPH_BUCKETS 16
+
+/* A set of captured decode graphs, one per batch-size bucket (opaque). */
+typedef struct gattn_decode_graphs gattn_decode_graphs;
+
+/*
+ * Decode graph bucket set (pegainfer "[Model] Gemma 4 M3 31B", Proposed Plan: the decode graph
+ * bucket set next to the split-KV chunk policy, and graph workspaces in the memory envelope).
+ * Captures, once, one HIP graph of gattn_decode per bucket size b: the call over the first b rows
+ * of the fixed buffers given here. A serving loop then refreshes those buffers (queries, page
+ * table, lengths) in place and replays the smallest bucket that holds its batch with
+ * gattn_decode_graphs_launch, which enqueues the captured kernels with no host-side argument
+ * work and no allocation.
+ *
+ *   layer .. split_tokens, workspace, out, lse  as for gattn_decode, sized for the largest
+ *              bucket: q, out [max_b][num_q_heads][head_dim], lse [max_b][num_q_heads],
+ *              page_table [max_b][pt_stride], ctx_lens [max_b], workspace at least
+ *              gattn_decode_workspace_bytes(layer, max_b, max_ctx, split_tokens) bytes. All
+ *              device memory, owned by the caller, which must keep it alive (and at the same
+ *              addresses) until gattn_decode_graphs_destroy.
+ *   buckets    n_buckets batch sizes, strictly increasing, each >= 1 (host memory, copied);
+ *              1 <= n_buckets <= GATTN_MAX_GRAPH_BUCKETS; max_b = buckets[n_buckets - 1].
+ *   graphs     receives the set (NULL on any error).
+ * The graphs are captured on a private stream of the current device and must be launched on a
+ * stream of the same device. Every argument is checked (as gattn_decode checks it, for each
+ * bucket) before anything is captured; a failure returns that status with nothing enqueued and
+ * nothing kept. A capture or instantiation failure returns GATTN_ERR_HIP.
+ */
+int gattn_decode_graphs_create(const gattn_layer *layer, const uint16_t *q, const uint16_t *k_pool,
+                               const uint16_t *v_pool, int64_t num_pages, const int32_t *page_table, int pt_stride,
+                               const int32_t *ctx_lens, int max_ctx, int split_tokens, void *workspace,
+                               size_t workspace_bytes, uint16_t *out, float *lse, const int32_t *buckets,
+                               int n_buckets, gattn_decode_graphs **graphs);
+
+/*
+ * The bucket a batch of `batch` rows runs in: the smallest bucket >= batch, or -1 if batch < 1,
+ * batch exceeds the largest bucket or graphs is NULL.
+ */
+int gattn_decode_graphs_bucket(const gattn_decode_graphs *graphs, int batch);
+
+/*
+ * Replays the graph of gattn_decode_graphs_bucket(graphs, batch) on `stream`. Rows batch ..
+ * bucket - 1 are computed too, from whatever the fixed buffers hold there: the caller either keeps
+ * them valid or sets their lengths to 0, which fails them closed (NaN outputs, no K/V read). The
+ * bits of rows 0 .. batch - 1 are those of gattn_decode over those rows alone. Launches of one set
+ * share its buffers: launches that overlap (other streams or host threads) race, and the caller
+ * orders them. Returns GATTN_ERR_NULL_PTR for a NULL set, GATTN_ERR_BAD_SHAPE when no bucket holds
+ * the batch, GATTN_ERR_HIP if the launch fails.
+ */
+int gattn_decode_graphs_launch(const gattn_decode_graphs *graphs, int batch, void *stream);
+
+/* Frees the set's graphs (after their launches have finished); NULL is ignored. */
+void gattn_decode_graphs_destroy(gattn_decode_graphs *graphs);
+
 /*
  * Chunked causal prefill (Core AI card, "Contents": a flash-prefill with a
  * query axis and an intra-chunk causal mask; "hybrid-pf64/ bundles": a prefill

@@ -1,6 +1,6 @@
 // Launch stubs for a host-only build of the library's C ABI (csrc/gattn.cpp), used by the CPU
 // sanitizer tests: argument validation, split planning and workspace sizing run for real under
-// AddressSanitizer and UndefinedBehaviorSanitizer, while every kernel launch fails with
+// AddressSanitizer and UndefinedBehaviorSanitizer, while every kernel launch and graph capture fails with
 // hipErrorInvalidValue (reported as GATTN_ERR_HIP), so this build can never compute a result.
 #include "kernels.h"
 
@@ -16,5 +16,15 @@ hipError_t launch_combine(int, int, int, int, const float *, const float *, uint
 hipError_t launch_prefill(const PrefillArgs &, int, bool, int, hipStream_t) { return hipErrorInvalidValue; }
 bool decode_merges_slots(int, bool, int, int64_t) { return false; }
 hipError_t noalloc_scratch(void **, size_t *) { return hipErrorInvalidValue; }
+hipError_t graph_capture_begin(hipStream_t *s) {
+    *s = nullptr;
+    return hipErrorInvalidValue;
+}
+hipError_t graph_capture_end(hipStream_t, void **exec) {
+    *exec = nullptr;
+    return hipErrorInvalidValue;
+}
+hipError_t graph_launch(void *, hipStream_t) { return hipErrorInvalidValue; }
+void graph_free(void *) {}
 
 }  // namespace gattn

@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported():
     assert names == sorted(["gattn_abi_version", "gattn_status_str", "gattn_layer_family", "gattn_kv_offset",
                             "gattn_decode_workspace_bytes", "gattn_decode", "gattn_decode_noalloc",
                             "gattn_decode_fp8kv", "gattn_prefill", "gattn_combine", "gattn_kv_append",
-                            "gattn_kv_append_fp8"])
+                            "gattn_kv_append_fp8", "gattn_decode_graphs_create", "gattn_decode_graphs_bucket",
+                            "gattn_decode_graphs_launch", "gattn_decode_graphs_destroy"])
     for n in names:
         assert hasattr(nat._lib, n), n
     assert g.gattn_abi_version() == 1
@@ -174,6 +175,53 @@ def test_decode_noalloc_rejects_bad_arguments_without_a_device(over, status):
     """The no-allocation decode checks its arguments exactly as gattn_decode does, and rejects a call
     whose partials would not fit its fixed scratch, all before any HIP call."""
     assert _noalloc_status(**over) == status
+
+
+def _graphs_status(**over):
+    lay = over.pop("layer", g.make_layer("global", 32, 4, 512))
+    args = dict(q=1 << 20, k_pool=2 << 20, v_pool=3 << 20, num_pages=100, page_table=4 << 20, pt_stride=512,
+                ctx_lens=5 << 20, max_ctx=8192, split_tokens=512, workspace=6 << 20, workspace_bytes=1 << 30,
+                out=7 << 20, lse=8 << 20, buckets=[1, 8, 32])
+    args.update(over)
+    try:
+        handle = g.gattn_decode_graphs_create(lay, **args)
+    except g.GattnError as e:
+        return e.status
+    g.gattn_decode_graphs_destroy(handle)
+    return 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(buckets=[]), nat.ERR_BAD_SHAPE),
+    (dict(buckets=list(range(1, 18))), nat.ERR_BAD_SHAPE),      # more than 16 buckets
+    (dict(buckets=[0, 8]), nat.ERR_BAD_SHAPE),
+    (dict(buckets=[8, 4]), nat.ERR_BAD_SHAPE),                   # not increasing
+    (dict(buckets=[4, 4]), nat.ERR_BAD_SHAPE),
+    (dict(q=None), nat.ERR_NULL_PTR),
+    (dict(v_pool=None), nat.ERR_NULL_PTR),
+    (dict(workspace=None), nat.ERR_NULL_PTR),
+    (dict(pt_stride=511), nat.ERR_BAD_SHAPE),
+    (dict(split_tokens=500), nat.ERR_BAD_SPLIT),
+    # the largest bucket sets the workspace: 32 rows need 32 x 32 x 16 x 513 x 4 B
+    (dict(workspace_bytes=g.gattn_decode_workspace_bytes(g.make_layer("global", 32, 4, 512), 8, 8192, 512)),
+     nat.ERR_WORKSPACE_TOO_SMALL),
+    (dict(layer=g.make_layer("global", 32, 4, 128)), nat.ERR_UNSUPPORTED),
+])
+def test_decode_graphs_reject_bad_arguments_without_a_device(over, status):
+    """The graph set checks its buckets and, for every bucket, the decode call it would capture,
+    all before any HIP call."""
+    assert _graphs_status(**over) == status
+
+
+def test_decode_graphs_null_handles():
+    assert g.gattn_decode_graphs_bucket(None, 4) == -1
+    with pytest.raises(g.GattnError) as e:
+        g.gattn_decode_graphs_launch(None, 4, stream=0)
+    assert e.value.status == nat.ERR_NULL_PTR
+    g.gattn_decode_graphs_destroy(None)
+    rc = nat._lib.gattn_decode_graphs_create(None, None, None, None, 0, None, 0, None, 0, 0, None, 0, None, None,
+                                             None, 0, None)
+    assert rc == nat.ERR_NULL_PTR
 
 
 def test_noalloc_scratch_limit():

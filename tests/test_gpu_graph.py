@@ -80,3 +80,49 @@ def test_graph_replays_match_eager(devio):
         for i, (d, _, _) in enumerate(calls):
             o, l = d.result()
             assert np.array_equal(o, eager[i][0]) and np.array_equal(l, eager[i][1]), (rep, i)
+
+
+@pytest.mark.parametrize("spec,split", [(workloads.GLOBAL_31B, 512), (workloads.GLOBAL_31B_KV_SHARED, 1024),
+                                        (workloads.LOCAL_31B, 512)], ids=["global", "global-kv-shared", "local"])
+def test_decode_graph_bucket_set(devio, spec, split):
+    """A bucket set {1, 4, 8, 16} captured over one fixed 16-row batch. For batches of 1, 3, 8, 11
+    and 16 rows the serving loop sets the lengths of the rows past the batch to 0 and replays the
+    smallest bucket that holds it, three times, each after eager work that overwrites the outputs.
+    The batch's rows equal gattn_decode over those rows alone, bit for bit, on every replay; the
+    padding rows inside the bucket fail closed (NaN), the rows past it are not written."""
+    import torch
+    from global_paged_gqa_amd import _native as nat
+    B, max_ctx, buckets = 16, 8192, [1, 4, 8, 16]
+    L = workloads.ragged((31, int(spec.kv_shared), int(spec.is_global)), 1, 6000, B)
+    b = workloads.make_batch(spec, L, np.ones(B, np.int32), (31, int(spec.kv_shared), int(spec.is_global)),
+                             back="visible", poison=True, pt_stride=max_ctx // 16)
+    d = devio.DeviceBatch(b)
+    need = nat.gattn_decode_workspace_bytes(d.layer, B, max_ctx, split)
+    ws = torch.full((max(need, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    h = nat.gattn_decode_graphs_create(d.layer, d.q, d.k_pool, d.v_pool, d.num_pages, d.page_table, d.pt_stride,
+                                       d.ctx_lens, max_ctx, split, ws, need, d.out, d.lse, buckets)
+    try:
+        for n in (1, 3, 8, 11, 16):
+            bucket = nat.gattn_decode_graphs_bucket(h, n)
+            assert bucket == min(x for x in buckets if x >= n)
+            ref = devio.DeviceBatch(b.subset(range(n)))
+            ref.decode(split, max_ctx)
+            ref_o, ref_l = ref.result()
+            lens = np.asarray(L, np.int32).copy()
+            lens[n:] = 0
+            d.ctx_lens.copy_(torch.from_numpy(lens).to("cuda"))
+            for rep in range(3):
+                d.out.fill_(7)              # eager work between the replays
+                d.lse.fill_(-3.0)
+                torch.cuda.synchronize()
+                nat.gattn_decode_graphs_launch(h, n)
+                o, l = d.result()
+                assert np.array_equal(o[:n], ref_o) and np.array_equal(l[:n], ref_l), (n, rep)
+                assert np.all(np.isnan(l[n:bucket])) and np.all(np.isnan(o[n:bucket])), (n, rep)
+                assert np.all(l[bucket:] == -3.0), (n, rep)
+        with pytest.raises(nat.GattnError) as e:
+            nat.gattn_decode_graphs_launch(h, B + 1)
+        assert e.value.status == nat.ERR_BAD_SHAPE
+    finally:
+        torch.cuda.synchronize()
+        nat.gattn_decode_graphs_destroy(h)
