@@ -414,20 +414,25 @@ def combine_time(torch, nat, d, split, stream, n=50):
 def sweep_extras(torch, devio, workloads, traffic, stream, layers, lays, kv_total, kv_fam, t_sweep, reps=10):
     """Per-family layer times, the sweep captured in a HIP graph, and the sweep over FP8 pools."""
     out = {}
+    # per-layer call times over five passes of the 60 layers; per family the median call (a single
+    # pass can catch a host-side stall between an event and its call)
     evs = []
-    for fam, d in layers:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        d.decode(workloads.SWEEP_SPLIT[fam])
-        e1.record(stream)
-        evs.append((fam, e0, e1))
+    for _ in range(5):
+        for fam, d in layers:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            d.decode(workloads.SWEEP_SPLIT[fam])
+            e1.record(stream)
+            evs.append((fam, e0, e1))
     torch.cuda.synchronize()
-    per = {"local": 0.0, "global": 0.0}
+    per = {"local": [], "global": []}
     for fam, e0, e1 in evs:
-        per[fam] += e0.elapsed_time(e1) * 1e-3
+        per[fam].append(e0.elapsed_time(e1) * 1e-3)
     for fam in ("local", "global"):
-        out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / per[fam] / 1e9, 1)
-        out[f"{fam}_layer_us"] = round(per[fam] / (50 if fam == "local" else 10) * 1e6, 2)
+        t_layer = median(per[fam])
+        n_layers = 50 if fam == "local" else 10
+        out[f"{fam}_layers_gbs"] = round(kv_fam[fam] / (t_layer * n_layers) / 1e9, 1)
+        out[f"{fam}_layer_us"] = round(t_layer * 1e6, 2)
 
     def sweep():
         for fam, d in layers:
@@ -533,13 +538,25 @@ def cfg2_measure(torch, devio, workloads, traffic, stream, flush, digest, steps=
     e1.record(stream)
     torch.cuda.synchronize()
     tc = e0.elapsed_time(e1) * 1e-3 / 50
+    # the same call replayed from the decode graph bucket set (buckets 8, 16, 32; the batch fills bucket 32)
+    max_ctx = int(batch.ctx_lens.max())
+    h = nat.gattn_decode_graphs_create(d.layer, d.q, d.k_pool, d.v_pool, d.num_pages, d.page_table, d.pt_stride,
+                                       d.ctx_lens, max_ctx, 512, d.workspace, d.ws_bytes, d.out, d.lse, [8, 16, 32])
+    try:
+        for _ in range(10):
+            nat.gattn_decode_graphs_launch(h, batch.B, stream)
+        tg = median(event_times(torch, stream, lambda: nat.gattn_decode_graphs_launch(h, batch.B, stream), steps))
+    finally:
+        torch.cuda.synchronize()
+        nat.gattn_decode_graphs_destroy(h)
     return batch, {"workload": "global decode: batch 32, 32 q heads, 4 KV heads, head_dim 512, contexts "
                                "~U{1..8192}, split 512", "kv_bytes": kv, "us": round(t * 1e6, 2),
                    "gbs": round(kv / t / 1e9, 1), "frac": round(kv / t / 1e9 / HBM_PEAK_GBS, 4),
                    "kernel": CFG2_KERNEL, "kernel_us": round((t - tc) * 1e6, 2),
                    "kernel_gbs": round(kv / (t - tc) / 1e9, 1), "combine_us": round(tc * 1e6, 2),
                    "traffic": measured_traffic(digest, "cfg2"),
-                   "mall_flushed_gbs": round(kv / tf / 1e9, 1), "mall_flushed_frac": round(kv / tf / 1e9 / HBM_PEAK_GBS, 4)}
+                   "mall_flushed_gbs": round(kv / tf / 1e9, 1), "mall_flushed_frac": round(kv / tf / 1e9 / HBM_PEAK_GBS, 4),
+                   "graph_bucket_us": round(tg * 1e6, 2), "graph_bucket_gbs": round(kv / tg / 1e9, 1)}
 
 
 def cpu_baselines(workloads, traffic, batches):
