@@ -90,12 +90,13 @@ __global__ __launch_bounds__(NS * W * 64) void decode_split_kernel(DecodeArgs a)
     // and keeps its own online-softmax state S_c. The states fold in stream order,
     // R = ((S_0 (+) S_1) (+) S_2) (+) S_3 (with two streams S_0 (+) S_1). W waves run the C streams,
     // E = C / W each, one after another: wave w runs streams w E .. w E + E - 1 and folds them in
-    // order in its registers; a wave whose first stream is not stream 0 first takes the fold of all
-    // earlier streams from the wave before it through LDS. Every launch shape thus applies the same
-    // operations to the same values, so it gives the same bits. NS > 1: the workgroup takes all NS
-    // split slots of its (row, KV head), one group of W waves per slot, and merges them itself.
-    // page streams of a split: four at head_dim 512 (one over FP8 pools, whose only launch shape
-    // is one wave per split), two at 256
+    // order in its registers. With one stream per wave the waves' states meet in LDS and each output
+    // element folds them in wave order; with two streams on each of two waves, wave 0 hands its fold
+    // to wave 1 through LDS. Every launch shape thus applies the same operations to the same values,
+    // so it gives the same bits. NS > 1: the workgroup takes all NS split slots of its (row, KV
+    // head), one group of W waves per slot, and merges them itself.
+    // Page streams of a split: four at head_dim 512 (one over FP8 pools, whose only launch shape is
+    // one wave per split), two at 256.
     constexpr int C = HD == 512 ? (F8 ? 1 : 4) : 2;
     constexpr int E = C / W;                    // streams per wave
     constexpr int kWaves = NS * W;
