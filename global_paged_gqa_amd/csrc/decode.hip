@@ -17,12 +17,12 @@
 // contiguous rate). The loads are non-temporal (every byte is read once) and go
 // straight to LDS, holding no registers.
 //
-// Work split. A split's pages form C page streams (four at head_dim 512, one there over FP8
-// pools, two at 256): stream c takes pages c, c+C, c+2C, ... and keeps its own online-softmax
-// state over the whole head dimension, and the states fold in stream order. A wave streams its
-// pages through its own slice of LDS (two or three K/V units ahead of the math, waited for with
-// explicit per-wave load counts, no barriers); a launch shape puts one, two or four streams on
-// each wave. Per page (16 tokens), in registers:
+// Work split. A split's pages form C page streams (at head_dim 512 four with K = V, two with
+// separate pools, one over FP8 pools; two at 256): stream c takes pages c, c+C, c+2C, ... and
+// keeps its own online-softmax state over the whole head dimension, and the states fold in stream
+// order. A wave streams its pages through its own slice of LDS (two or three K/V units ahead of
+// the math, waited for with explicit per-wave load counts, no barriers); a launch shape puts one,
+// two or four streams on each wave. Per page (16 tokens), in registers:
 //   S^T[16 tok][16 heads] = K[tok][:] . Q^T[:][heads]    (MFMA 16x16x32, A = K read
 //                                                         from LDS, B = Q^T in registers)
 //   online softmax on S^T columns                         (VALU, lane swaps)
@@ -95,9 +95,10 @@ __global__ __launch_bounds__(NS * W * 64) void decode_split_kernel(DecodeArgs a)
     // to wave 1 through LDS. Every launch shape thus applies the same operations to the same values,
     // so it gives the same bits. NS > 1: the workgroup takes all NS split slots of its (row, KV
     // head), one group of W waves per slot, and merges them itself.
-    // Page streams of a split: four at head_dim 512 (one over FP8 pools, whose only launch shape is
-    // one wave per split), two at 256.
-    constexpr int C = HD == 512 ? (F8 ? 1 : 4) : 2;
+    // Page streams of a split: four at head_dim 512 with K = V, two with separate K and V pools (whose
+    // waves carry twice the bytes per page), one over FP8 pools (whose only launch shape is one wave
+    // per split); two at 256.
+    constexpr int C = HD == 512 ? (F8 ? 1 : (SHARED ? 4 : 2)) : 2;
     constexpr int E = C / W;                    // streams per wave
     constexpr int kWaves = NS * W;
     constexpr int kThreads = kWaves * 64;
@@ -692,13 +693,14 @@ __global__ __launch_bounds__(NS * W * 64) void decode_split_kernel(DecodeArgs a)
 }
 
 // Launch shape per head_dim, measured on the decode workloads of both families. head_dim 512
-// (16 KB units): a batch of more than two workgroups per CU runs one wave per workgroup (all four
-// page streams of its split in turn) with two units in flight, four workgroups per CU, so that a
+// (16 KB units): a batch of more than two workgroups per CU runs one wave per workgroup (all page
+// streams of its split in turn) with two units in flight, four workgroups per CU, so that a
 // batch's (row, KV head, split) items mostly start at once and no CU waits on a partly filled
-// last round. A grid of at most one workgroup per CU (one long row, say) runs the four streams on
-// four waves, and up to two workgroups per CU (a batch of a single-KV-head family) on two waves of
-// two streams each: there one wave working through a split's pages one at a time would set the
-// pace. head_dim 256 (8 KB units): the two page streams on two waves with three units each, three
+// last round. With K = V a grid of at most one workgroup per CU (one long row, say) runs the four
+// streams on four waves, and up to two workgroups per CU on two waves of two streams each; with
+// separate pools a grid of up to two workgroups per CU (a batch of a single-KV-head family) runs
+// its two streams on two waves: there one wave working through a split's pages one at a time
+// would set the pace. head_dim 256 (8 KB units): the two page streams on two waves with three units each, three
 // workgroups per CU, which keeps the window-sized local items (at most 1024 keys) from running
 // one page at a time on few waves. Every shape gives the same bits.
 template <int HD>
@@ -732,9 +734,11 @@ hipError_t launch(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
     }
     if constexpr (HD == 512) {
         const int64_t items = (int64_t)grid.x * grid.y * grid.z;
-        if (items <= kNumCUs)
-            return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 4, SLICE>, grid, dim3(4 * 64), args,
-                                   0, stream);
+        if constexpr (SHARED) {
+            if (items <= kNumCUs)
+                return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 4, SLICE>, grid, dim3(4 * 64),
+                                       args, 0, stream);
+        }
         if (items <= 2 * kNumCUs)
             return hipLaunchKernel((const void *)decode_split_kernel<HD, SHARED, 2, SLICE>, grid, dim3(2 * 64), args,
                                    0, stream);

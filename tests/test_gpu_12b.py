@@ -2,8 +2,8 @@
 
 Global family: 16 query heads over a single KV head (g = 16, head_dim 512), the degenerate
 block-GQA case where a row's parallelism comes only from its splits. Local family: 16 query
-heads over 8 KV heads, head_dim 256, window 1024. Decode at small and full batch (the full batch
-runs a split's four page streams on two waves, the small ones on four), chunked prefill on small
+heads over 8 KV heads, head_dim 256, window 1024. Decode at small and full batch (both run a
+split's two page streams on two waves), chunked prefill on small
 ragged rows and on the 12B mixed step's prefill rows (sampled queries).
 """
 import numpy as np

@@ -173,9 +173,9 @@ def test_bitwise_batch_invariance_and_reorder(devio):
 
 @pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "global-kv-shared"])
 def test_bitwise_launch_shape_invariance(devio, spec):
-    """A head_dim 512 grid of at most 256 (row, KV head, split) items runs a split's four page
-    streams on four waves, one each; up to 512 items on two waves of two streams; a larger grid
-    on one wave that runs the four in turn. A row gives the same bits in every shape:
+    """A head_dim 512 grid of at most 256 (row, KV head, split) items runs a split's page streams
+    on one wave each (four with K = V, two with separate pools); up to 512 items on two waves; a
+    larger grid on one wave that runs the streams in turn. A row gives the same bits in every shape:
     alone, in 2- and 4-row batches (16 x 4 x 4 = 256 items at most), in a 6-row batch (384 items)
     and inside a 10-row batch (640 items). The small-grid results also match the oracle."""
     L = workloads.ragged((14, int(spec.kv_shared)), 1, 8192, 10)
@@ -192,11 +192,12 @@ def test_bitwise_launch_shape_invariance(devio, spec):
 
 @pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.GLOBAL_31B_KV_SHARED], ids=["global", "global-kv-shared"])
 def test_page_stream_edges(devio, spec):
-    """Splits of 128 keys (eight pages, two per page stream at head_dim 512) with every page count
-    from one to eight in the last split, so that one, two or three of the four streams are empty or
-    one page short, and a poisoned (NaN) pool behind every unused slot. Each row alone runs the
-    four-wave shape (256 items), two rows the two-wave shape, all thirteen the one-wave shape; every
-    row gives the same bits in all three and matches the oracle."""
+    """Splits of 128 keys (eight pages) with every page count from one to eight in the last split,
+    so that page streams are empty or one page short (four streams with K = V, two with separate
+    pools), and a poisoned (NaN) pool behind every unused slot. Each row alone runs the four-wave
+    shape with K = V and the two-wave shape otherwise (256 items), two rows the two-wave shape, all
+    thirteen the one-wave shape; every row gives the same bits in every shape and matches the
+    oracle."""
     L = np.array([1, 16, 17, 33, 49, 64, 65, 90, 100, 113, 128, 8192 - 7, 8192], np.int32)
     b = workloads.make_batch(spec, L, np.ones(len(L), np.int32), (17, int(spec.kv_shared)), back="all", poison=True)
     o_all, l_all = _run(devio, b, 128, max_ctx=8192)
@@ -364,7 +365,7 @@ def _probe_batch(spec, t_star, key, n_filler=0, pt_stride=None, code_of=None):
 
 
 HD512_SHAPES = {  # name: (kv_shared, split, filler rows, max_ctx, pt_stride) -> items = slots * 4 * rows
-    "global-4waves": (False, 512, 0, None, None),            # 6 x 4 = 24 items
+    "global-2waves-small": (False, 512, 0, None, None),      # 6 x 4 = 24 items
     "global-2waves": (False, 512, 1, 20000, 1250),           # 40 x 4 x 2 = 320 items
     "global-1wave": (False, 512, 8, 8192, 512),               # 16 x 4 x 9 = 576 items
     "kv-shared-4waves": (True, 1024, 0, None, None),         # 3 x 4 = 12 items
@@ -375,10 +376,10 @@ HD512_SHAPES = {  # name: (kv_shared, split, filler rows, max_ctx, pt_stride) ->
 
 @pytest.mark.parametrize("shape", list(HD512_SHAPES))
 def test_position_probe_hd512(devio, shape):
-    """The position probe at head_dim 512 in each launch shape of the global family (a split's
-    four page streams on four waves, on two waves of two streams, or on one wave in turn; separate
-    pools and K=V), swept over page, split and stream edges: the output must be V[t*] bit for bit
-    in every head."""
+    """The position probe at head_dim 512 in each launch shape of the global family (with K = V a
+    split's four page streams on four waves, on two waves of two streams, or on one wave in turn;
+    with separate pools its two streams on two waves or on one), swept over page, split and stream
+    edges: the output must be V[t*] bit for bit in every head."""
     shared, split, n_fill, max_ctx, pt_stride = HD512_SHAPES[shape]
     spec = workloads.LayerSpec("global", 32, 4, 512, kv_shared=shared, scale=1.0)
     for t_star in PROBE_T:
