@@ -197,8 +197,8 @@ def append_measure(torch, devio, workloads, stream, flush, iters=20):
     """gattn_kv_append of one mixed step's new tokens (the 4 x 2048 prefill chunks and the 60 decode
     tokens, all 64 rows in one call) for each 31B family: GB/s of algorithmic bytes, every new K and
     V element read once and written once; each timed run after a MALL flush. Beside it, a plain
-    device copy of the same bytes under the same flush (torch's copy of K and V into contiguous
-    buffers): the practical ceiling of a transfer of this size."""
+    device copy of the same bytes under the same flush (one torch copy of K and V, stacked, into a
+    contiguous buffer): the practical ceiling of a transfer of this size."""
     import numpy as np
     out = {}
     for fam in ("global", "local"):
@@ -209,18 +209,17 @@ def append_measure(torch, devio, workloads, stream, flush, iters=20):
         n_new = b.q_lens.astype(np.int32)
         cu = devio.dev(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32))
         T, mx = int(n_new.sum()), int(n_new.max())
-        kn = torch.randn(T, s.num_kv_heads, s.head_dim, device="cuda").to(torch.bfloat16).view(torch.int16)
-        vn = torch.randn_like(kn, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        kvn = torch.randn(2, T, s.num_kv_heads, s.head_dim, device="cuda").to(torch.bfloat16).view(torch.int16)
+        kn, vn = kvn[0], kvn[1]
         nbytes = kn.numel() * 2 * 2 * 2  # K and V, read and written
 
         def call():
             devio.nat.gattn_kv_append(d.layer, kn, vn, d.k_pool, d.v_pool, d.num_pages, d.page_table, d.pt_stride,
                                       cu, d.ctx_lens, b.B, mx, None)
-        ck, cv = torch.empty_like(kn), torch.empty_like(vn)
+        ckv = torch.empty_like(kvn)
 
-        def copy():
-            ck.copy_(kn)
-            cv.copy_(vn)
+        def copy():  # one launch over K and V (stacked), as the append is one launch
+            ckv.copy_(kvn)
         for _ in range(5):
             call()
             copy()
@@ -229,7 +228,7 @@ def append_measure(torch, devio, workloads, stream, flush, iters=20):
         out[fam] = {"tokens": T, "rows": b.B, "bytes": nbytes, "us": round(t * 1e6, 2),
                     "gbs": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                     "plain_copy_us": round(tc * 1e6, 2), "plain_copy_gbs": round(nbytes / tc / 1e9, 1)}
-        del ck, cv
+        del ckv
         if fam == "local":  # the same tokens into E4M3 pools: 2 bytes read and 1 written per element
             k8 = torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")
             v8 = torch.zeros(d.k_pool.shape, dtype=torch.uint8, device="cuda")
@@ -243,7 +242,7 @@ def append_measure(torch, devio, workloads, stream, flush, iters=20):
             t8 = median(event_times(torch, stream, call8, iters, flush))
             out["local_fp8"] = {"bytes": nbytes8, "us": round(t8 * 1e6, 2), "gbs": round(nbytes8 / t8 / 1e9, 1)}
             del k8, v8
-        del d, kn, vn
+        del d, kn, vn, kvn
         torch.cuda.empty_cache()
     out["workload"] = ("gattn_kv_append of the mixed step's 8252 new tokens per family (4 prefill chunks of 2048 and "
                        "60 decode tokens, one call over the 64 rows) into the 31B pools")
