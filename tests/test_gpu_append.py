@@ -73,10 +73,12 @@ def test_kv_append_bitwise(devio, spec):
         assert np.array_equal(vp, ref_v)
 
 
-def test_kv_append_fails_closed(devio):
+@pytest.mark.parametrize("spec", [workloads.GLOBAL_31B, workloads.LOCAL_31B], ids=["global", "local"])
+def test_kv_append_fails_closed(devio, spec):
     """Out-of-range and -1 page ids, positions beyond the table and rows with more new tokens
-    than cached ones write nothing and raise the status flag; every other token is written."""
-    spec = workloads.GLOBAL_31B
+    than cached ones write nothing and raise the status flag; every other token is written. (At
+    head_dim 256 the kernel reads a token's source row before its page id, at 512 after: both
+    orders are covered.)"""
     b, L, n_new, cu, k_new, v_new = _case(spec, (42, 0))
     pt = b.page_table.copy()
     pt[2, 0] = b.num_pages + 5           # row 2 has no new tokens: never read, no flag from it
