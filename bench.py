@@ -603,7 +603,7 @@ def cpu_baselines(workloads, traffic, batches):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
               "path: rows shard across GPUs with no attention-side communication.", file=sys.stderr)
         sys.exit(2)
     cpu_model = host_cpu_model()

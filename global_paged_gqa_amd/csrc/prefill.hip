@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // No ring load (the zero-filling ones past the last block included) may still be writing
     // this workgroup's LDS when it ends.
     wait_vmcnt<0>();
-    // the tile's verdict on its page ids, from every wave's pages
+    // whether any wave of the tile met a bad page id
     auto bad_tile = [&](int mine) {
         if (mine)
             sm_bad = 1;

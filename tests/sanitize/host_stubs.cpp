@@ -1,7 +1,7 @@
 // Launch stubs for a host-only build of the library's C ABI (csrc/gattn.cpp), used by the CPU
 // sanitizer tests: argument validation, split planning and workspace sizing run for real under
 // AddressSanitizer and UndefinedBehaviorSanitizer, while every kernel launch and graph capture fails with
-// hipErrorInvalidValue (reported as GATTN_ERR_HIP), so this build can never compute a result.
+// hipErrorInvalidValue (reported as GATTN_ERR_HIP), so a library linked with them never computes a result.
 #include "kernels.h"
 
 namespace gattn {
