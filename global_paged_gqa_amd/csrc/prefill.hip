@@ -558,8 +558,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto sm_step = [&](int step, SmState &z, f32x16 &st, u32x4 (&pf)[2], float &alpha, int r) {
         if (step < 4) {
             // raw scores: the scale enters the exponent (step 5-8) and the row maximum (step 4);
-            // on edge blocks the invisible keys become -inf
-            if (!z.interior) {
+            // on edge blocks the invisible keys become -inf. With two row tiles (head_dim 256) every
+            // block takes the compare (a no-op inside the visible range): the branches would cut the
+            // product's MFMAs into short runs that the softmax steps cannot be scheduled across
+            // (measured 1-3% faster); at 512 the branch still pays for itself.
+            if (RT == 2 || !z.interior) {
 #pragma unroll
                 for (int v = 4 * step; v < 4 * step + 4; ++v)
                     st[v] = z.vis0 + (uint32_t)(8 * (v >> 2) + (v & 3)) <= z.span ? st[v] : -INFINITY;
