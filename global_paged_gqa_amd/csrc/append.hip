@@ -58,10 +58,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
     constexpr int CPR = HD / 8;           // 16-byte chunks per (token, kv_head) row
     constexpr int RPI = kThreads / CPR;   // rows a workgroup copies per step
     constexpr int kUnroll = unroll(HD);
-    // At head_dim 256 a workgroup's rows take four passes of the loop below; reading each source row
-    // before its table entry (a token with a bad page id is then read and not written) lets the two
-    // loads overlap in every pass (5% on the mixed step's local append). At 512 one pass covers the
-    // workgroup, and the table entry goes first (the other order measured 1-3% slower).
+    // At head_dim 256 a workgroup's rows take several passes of the loop below (four with 16 KV
+    // heads); reading each source row before its table entry (a token with a bad page id is then
+    // read and not written) lets the two loads overlap in every pass (5% on the mixed step's local
+    // append). At 512 one pass covers a workgroup of up to four KV heads, and the table entry goes
+    // first (the other order measured 1-3% slower).
     constexpr bool kSrcFirst = HD == 256;
     const int r = blockIdx.y;
     const int n0 = a.cu_new[r], n = a.cu_new[r + 1] - n0;
